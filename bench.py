@@ -1,0 +1,322 @@
+"""Benchmark of the FP8 wire codec's hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step is one pass of the whole hot path over the workload, all inputs
+already resident in HBM:
+  1. block-128 e4m3 quantize of the Pi0.5-scale bf16 gradient
+     (3.5e9 elements, ~7 GB; 27,343,750 fp32 scales);
+  2. fused dequant-reduce of 8 peer shards of 437,500,000 elements into fp32
+     (each shard the block quantize of that peer's gradient slice);
+  3. MXFP8 quantize of one Qwen3-30B-A3B-shaped MoE layer (128 experts:
+     gate and up [768, 2048], down [2048, 768]; three launches).
+`value` is the step's bf16-equivalent bytes (2 B per quantized element, 2 B
+per element of every reduced peer) divided by the step time.
+
+Per-launch kernel times come from HIP events recorded on the stream the
+kernels run on (torch's current stream); the roofline figure uses the
+dominant kernel (the 7 GB quantize) with its algorithmic HBM bytes
+(2 + 1 + 4/128 B per element).  Side figures (not in the step): the
+dequantize alone, and the naive dequantize-then-sum path that the fused
+kernel replaces.  The CPU baseline times the oracle (single-threaded C) on a
+bounded sample of the same workload.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantize & dequant-reduce GB/s (bf16-equiv) and % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+QUANT_BYTES_PER_ELEM = 2 + 1 + 4 / 128
+MX_BYTES_PER_ELEM = 2 + 1 + 1 / 32
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+QUANT_KERNEL_SRC = os.path.join(ROOT, "dequantize_reduce_transfer_amd", "csrc", "quantize.hip")
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def reduce_bytes_per_elem(k, out_bytes):
+    return k * (1 + 4 / 128) + out_bytes
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(kernel_src):
+    """HBM traffic per dispatch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, "quantize_pi05_e4m3_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and not line.startswith("#"):
+                vals[parts[0]] = parts[1]
+    if vals.get("source_sha256") != source_digest(kernel_src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events around each launch on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name):
+        ev = self.pairs.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev))
+
+    def reset(self):
+        self.pairs = {}
+
+
+def cpu_baseline(x, peers, moe, frac, fmt):
+    """The oracle, as it stands, on the first `frac` of every input."""
+    import numpy as np
+    import oracle
+    from dequantize_reduce_transfer_amd import workloads
+
+    n_q = int(x.numel() * frac) // 128 * 128
+    xs = workloads.bits(x[:n_q])
+    n_r = int(peers[0][0].numel() * frac) // 128 * 128
+    qs = [q[:n_r].cpu().numpy() for q, _ in peers]
+    ss = [s[: n_r // 128].cpu().numpy() for _, s in peers]
+    e_mx = max(1, int(moe["gate"].shape[0] * frac))
+    ws = {k: workloads.bits(v[:e_mx]).reshape((-1, v.shape[-1])) for k, v in moe.items()}
+    t0 = time.perf_counter()
+    oracle.quantize(xs, fmt)
+    oracle.dequant_reduce(qs, ss, fmt)
+    for w in ws.values():
+        oracle.mx8_quantize(w)
+    dt = time.perf_counter() - t0
+    bf16_bytes = 2 * n_q + 2 * len(qs) * n_r + sum(2 * w.size for w in ws.values())
+    return {
+        "value": round(bf16_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("first %.4g of each input: quantize %d elements, dequant-reduce k=%d x %d "
+                   "elements, mx8 %d experts of each of 3 tensors; %.1f s of single-threaded "
+                   "oracle work" % (frac, n_q, len(qs), n_r, e_mx, dt)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-frac", type=float, default=1 / 16,
+                    help="fraction of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side", action="store_true", help="skip the naive-path side figures")
+    ap.add_argument("--copy-reference-gib", type=float, default=1.0,
+                    help="size of the plain device copy run once for counter calibration")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU: this build has no multi-GPU path "
+                         "(got --gpus %d). Run with --gpus 1.\n" % args.gpus)
+        sys.exit(2)
+
+    import torch
+
+    import dequantize_reduce_transfer_amd as fq
+    from dequantize_reduce_transfer_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fmt = fq.E4M3
+    n = workloads.PI05_N
+    k = workloads.PI05_PEERS
+    n_shard = workloads.PI05_SHARD_N
+
+    log("generating the %.2e-element bf16 gradient on the GPU" % n)
+    x = workloads.segmented_gradient(n, seed=0, device=dev)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.empty(fq.num_scales(n), dtype=torch.float32, device=dev)
+
+    log("generating %d peer shards of %d elements and quantizing them" % (k, n_shard))
+    peers = []
+    for p in range(k):
+        g = workloads.pi05_peer_shard(p, n_shard, device=dev)
+        peers.append(fq.fp8q_quantize(g, fmt))
+        del g
+    y = torch.empty(n_shard, dtype=torch.float32, device=dev)
+    qs = [a for a, _ in peers]
+    ss = [b for _, b in peers]
+
+    log("generating the MoE layer")
+    moe = workloads.moe_layer(seed=0, device=dev)
+    mx_out = {name: (torch.empty(w.shape, dtype=torch.uint8, device=dev),
+                     torch.empty((w.numel() // w.shape[-1], w.shape[-1] // 32),
+                                 dtype=torch.uint8, device=dev)) for name, w in moe.items()}
+    n_mx = sum(w.numel() for w in moe.values())
+
+    # one plain device copy of known size, for calibrating HBM byte counters
+    if args.copy_reference_gib > 0:
+        nb = int(args.copy_reference_gib * (1 << 30))
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    timer = Timer(torch)
+
+    def step():
+        timer.run("quantize", lambda: fq.fp8q_quantize(x, fmt, q_out=q, scales_out=s))
+        timer.run("dequant_reduce", lambda: fq.fp8q_dequant_reduce(qs, ss, fmt, out=y))
+        for name, w in moe.items():
+            qo, eo = mx_out[name]
+            timer.run("mx8_" + name, lambda w=w, qo=qo, eo=eo: fq.mx8_quantize(w, q_out=qo, e8m0_out=eo))
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.reset()
+
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+
+    bf16_bytes_step = 2 * n + 2 * k * n_shard + 2 * n_mx
+    value = bf16_bytes_step / (elapsed / args.steps) / 1e9
+
+    ops = {}
+    q_ms = timer.mean_ms("quantize")
+    r_ms = timer.mean_ms("dequant_reduce")
+    q_alg = QUANT_BYTES_PER_ELEM * n
+    r_alg = reduce_bytes_per_elem(k, 4) * n_shard
+    ops["quantize_e4m3"] = {"elements": n, "us": round(q_ms * 1e3, 2),
+                            "bf16_equiv_GBps": round(2 * n / q_ms / 1e6, 1),
+                            "hbm_GBps": round(q_alg / q_ms / 1e6, 1),
+                            "frac_peak": round(q_alg / q_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    ops["dequant_reduce_k8_f32"] = {"elements": n_shard, "us": round(r_ms * 1e3, 2),
+                                    "bf16_equiv_GBps": round(2 * k * n_shard / r_ms / 1e6, 1),
+                                    "hbm_GBps": round(r_alg / r_ms / 1e6, 1),
+                                    "frac_peak": round(r_alg / r_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    mx_ms = 0.0
+    for name, w in moe.items():
+        ms = timer.mean_ms("mx8_" + name)
+        mx_ms += ms
+        alg = MX_BYTES_PER_ELEM * w.numel()
+        ops["mx8_" + name] = {"elements": w.numel(), "us": round(ms * 1e3, 2),
+                              "hbm_GBps": round(alg / ms / 1e6, 1),
+                              "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    ops["mx8_layer"] = {"elements": n_mx, "us": round(mx_ms * 1e3, 2),
+                        "hbm_GBps": round(MX_BYTES_PER_ELEM * n_mx / mx_ms / 1e6, 1),
+                        "frac_peak": round(MX_BYTES_PER_ELEM * n_mx / mx_ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+    side = {}
+    if not args.no_side:
+        log("side figures: dequantize alone and the naive dequantize-then-sum")
+        parts = [torch.empty(n_shard, dtype=torch.float32, device=dev) for _ in range(k)]
+        t2 = Timer(torch)
+        for it in range(3 + 10):
+            if it == 3:
+                torch.cuda.synchronize()
+                t2.reset()
+            for p in range(k):
+                t2.run("dequantize", lambda p=p: fq.fp8q_dequantize(qs[p], ss[p], fmt, out=parts[p]))
+            t2.run("sum", lambda: fq.fp8q_sum_f32(parts, out=y))
+        torch.cuda.synchronize()
+        d_ms = t2.mean_ms("dequantize")
+        naive_ms = k * d_ms + t2.mean_ms("sum")
+        d_alg = reduce_bytes_per_elem(1, 4) * n_shard
+        side["dequantize_f32"] = {"elements": n_shard, "us": round(d_ms * 1e3, 2),
+                                  "hbm_GBps": round(d_alg / d_ms / 1e6, 1),
+                                  "frac_peak": round(d_alg / d_ms / 1e6 / HBM_PEAK_GBS, 4)}
+        side["naive_dequant_then_sum_k8_us"] = round(naive_ms * 1e3, 2)
+        side["fused_speedup_vs_naive"] = round(naive_ms / r_ms, 2)
+        del parts
+
+    roofline = {
+        "bound": "hbm",
+        "kernel": "quantize_kernel<E4M3> (block-128 quantize, 3.5e9 elements)",
+        "achieved": round(q_alg / q_ms / 1e6, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(q_alg / q_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "traffic": read_traffic(QUANT_KERNEL_SRC),
+        "algorithmic_bytes_per_launch": q_alg,
+        "avg_launch_us": round(q_ms * 1e3, 2),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "pi05_gradient_fp8_wire_step",
+            "quantize": "block-128 e4m3, 3,500,000,000 bf16 elements (segments of 25M, "
+                        "std log-uniform 1e-6..1e-2)",
+            "dequant_reduce": "k=8 peer shards x 437,500,000 elements -> fp32",
+            "mx8": "Qwen3-30B-A3B MoE layer, 128 experts, gate/up [768,2048], down [2048,768]",
+            "bf16_equiv_bytes_per_step": bf16_bytes_step,
+        },
+        "roofline": roofline,
+        "ops": ops,
+        "side": side,
+    }
+
+    if not args.no_cpu_baseline:
+        log("CPU baseline: oracle on %.4g of the workload" % args.cpu_frac)
+        moe_cpu = {name: w for name, w in moe.items()}
+        out["cpu_baseline"] = cpu_baseline(x, peers, moe_cpu, args.cpu_frac, fmt)
+    else:
+        out["cpu_baseline"] = None
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

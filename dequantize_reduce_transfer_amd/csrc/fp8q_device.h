@@ -1,0 +1,113 @@
+// fp8q_device.h -- gfx950 device helpers shared by the codec's kernels.
+//
+// Wave64 only.  Cross-lane reductions use DPP (no LDS); FP8 conversions use
+// the CDNA4 packed conversion instructions, which implement the OCP E4M3 /
+// E5M2 formats with round-to-nearest-even (the default MODE rounding).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 128;      // elements per fp32 scale
+constexpr int kMxBlock = 32;     // elements per E8M0 scale
+
+// DPP control words (CDNA DPP encodings).
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
+// Max over the 4 lanes of a quad: every lane gets the result.
+__device__ __forceinline__ uint32_t max_quad(uint32_t v) {
+  v = dpp_max<kDppQuadXor1>(v);
+  return dpp_max<kDppQuadXor2>(v);
+}
+
+// Max over a row of 16 lanes: every lane gets the result.
+__device__ __forceinline__ uint32_t max_row16(uint32_t v) {
+  v = max_quad(v);
+  v = dpp_max<kDppRowHalfMirror>(v);
+  return dpp_max<kDppRowMirror>(v);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest sign-cleared bf16 bit pattern among the 8 bf16 held in a uint4.
+// For finite values this is the bit pattern of max |x|; inf / NaN patterns
+// (>= 0x7F80) order above every finite one.
+__device__ __forceinline__ uint32_t amax_bits8(uint4 v) {
+  const uint32_t m = 0x7FFF7FFFu;
+  u16x2 a = __builtin_bit_cast(u16x2, v.x & m);
+  u16x2 b = __builtin_bit_cast(u16x2, v.y & m);
+  u16x2 c = __builtin_bit_cast(u16x2, v.z & m);
+  u16x2 d = __builtin_bit_cast(u16x2, v.w & m);
+  u16x2 r = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                      __builtin_elementwise_max(c, d));
+  uint32_t lo = r.x, hi = r.y;
+  return lo > hi ? lo : hi;
+}
+
+// The two bf16 halves of a dword as fp32 (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Pack four fp32 values into four FP8 codes (byte i <- value i).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  uint32_t r;
+  if constexpr (FMT == 0) {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
+  } else {
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, (int)r, true);
+  }
+  return r;
+}
+
+// Decode FP8 codes 0,1 (HI = false) or 2,3 (HI = true) of a dword to fp32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int FMT, bool HI>
+__device__ __forceinline__ f32x2 dec2(uint32_t w) {
+  if constexpr (FMT == 0)
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  else
+    return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
+}
+
+template <int FMT>
+__device__ __forceinline__ float fp8_max() {
+  return FMT == 0 ? 448.0f : 57344.0f;
+}
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  __bf16 x = (__bf16)a;
+  __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(unsigned short, x) |
+         ((uint32_t)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+// Wave-uniform value (the compiler can keep it in an SGPR).
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Global wave index and wave count of a 1-D launch of 256-thread workgroups.
+__device__ __forceinline__ uint32_t wave_index() {
+  return uniform(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+}
+__device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (blockDim.x / kWave); }
+
+}  // namespace fp8q

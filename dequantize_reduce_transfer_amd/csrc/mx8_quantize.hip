@@ -1,0 +1,131 @@
+// mx8_quantize.hip -- MXFP8 (E4M3 codes + E8M0 scale per 32 along K)
+// weight quantize on gfx950.
+//
+// Method ("perf: Reduce MXFP8 refit weight-transfer overheads", sections
+// "Summary" and "Safety", and the review's "Verified clean" list: trainer
+// weights prequantized to E4M3 with an E8M0 scale per 32 elements, the
+// zero-scale clamp, scales shaped [rows, K/32]; the scale rule is the OCP MX
+// v1.0 one):
+//   X = clamp(floor(log2 amax) - 8, -127, 127),  code = X + 127,
+//   q_i = satRNE_e4m3(x_i * 2^-X).
+// For a finite bf16 amax with exponent field e, floor(log2 amax) - 8 >= -127
+// exactly when e >= 8, and every bf16 subnormal falls below that, so
+//   code = max(e, 8) - 8
+// with no logarithm at all; 2^-X = 2^(127 - code) is built from its bits.
+// x * 2^-X is exact wherever the result can matter (below 2^-126 it encodes
+// to zero either way); the clamp to +-448 then turns the hardware's RNE
+// conversion into the saturating one for the values in (448, 512).
+//
+// Layout.  With K a multiple of 32 the [rows, K] tensor is a flat sequence
+// of 32-element blocks and the [rows, K/32] scale array is that sequence's
+// block order, so the kernel never needs rows or K.  A block is 64 bytes = a
+// quad of lanes x 16 B; one wave-wide 16-byte load covers 16 blocks (1 KiB
+// contiguous) and the block amax takes 2 DPP steps.  A tile is U loads (16U
+// blocks); lane 4g + c stores the E8M0 byte of block (u = c, g), so one byte
+// store per lane writes the tile's 16U scale bytes contiguously.
+#include "fp8q_device.h"
+#include "launch.h"
+
+namespace fp8q {
+namespace {
+
+constexpr int kMxU = 4;            // 1 KiB loads in flight per wave per tile (<= 4)
+constexpr int kWgPerCu = 8;
+
+struct MxScale {
+  uint32_t code;   // E8M0 byte
+  float mul;       // 2^-X
+  bool finite;
+};
+
+__device__ __forceinline__ MxScale mx_scale(uint32_t amax_bits) {
+  MxScale m;
+  const uint32_t e = amax_bits >> 7;
+  m.finite = amax_bits < 0x7F80u;
+  const uint32_t code = e > 8u ? e - 8u : 0u;
+  m.code = m.finite ? code : 0xFFu;
+  m.mul = __uint_as_float((254u - code) << 23);      // 2^(127 - code)
+  return m;
+}
+
+__device__ __forceinline__ float mx_q(float x, float mul) {
+  return __builtin_amdgcn_fmed3f(x * mul, -448.0f, 448.0f);
+}
+
+__device__ __forceinline__ uint2 mx_quant8(uint4 v, const MxScale &m) {
+  uint2 r;
+  r.x = cvt4<0>(mx_q(bf16_lo(v.x), m.mul), mx_q(bf16_hi(v.x), m.mul), mx_q(bf16_lo(v.y), m.mul),
+                mx_q(bf16_hi(v.y), m.mul));
+  r.y = cvt4<0>(mx_q(bf16_lo(v.z), m.mul), mx_q(bf16_hi(v.z), m.mul), mx_q(bf16_lo(v.w), m.mul),
+                mx_q(bf16_hi(v.w), m.mul));
+  if (!m.finite) {
+    r.x = 0x7F7F7F7Fu;
+    r.y = 0x7F7F7F7Fu;
+  }
+  return r;
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void mx8_kernel(const uint4 *__restrict__ w, uint2 *__restrict__ q,
+                                                  uint8_t *__restrict__ e8m0, uint64_t nchunks,
+                                                  uint64_t full_tiles) {
+  constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
+  constexpr uint64_t kBlocks = U * 16;             // 32-element blocks per tile
+  const uint32_t lane = lane_id();
+  const uint32_t g = lane >> 2, c = lane & 3;
+  const uint64_t nw = wave_count();
+  const uint64_t w0 = wave_index();
+
+  for (uint64_t t = w0; t < full_tiles; t += nw) {
+    const uint64_t c0 = t * kChunks;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = w[c0 + u * kWave + lane];
+    uint32_t codes[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const MxScale m = mx_scale(max_quad(amax_bits8(v[u])));
+      q[c0 + u * kWave + lane] = mx_quant8(v[u], m);
+      codes[u] = m.code;
+    }
+    if (c < U) {
+      uint32_t code = codes[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) code = (c == (uint32_t)u) ? codes[u] : code;
+      e8m0[t * kBlocks + c * 16 + g] = (uint8_t)code;
+    }
+  }
+  // Tail: whole blocks only (the element count is a multiple of 32, so every
+  // quad of chunks is either entirely present or entirely absent).
+  if (w0 == nw - 1) {
+    for (uint64_t base = full_tiles * kChunks; base < nchunks; base += kWave) {
+      const uint64_t chunk = base + lane;
+      const bool valid = chunk < nchunks;
+      const uint4 v = valid ? w[chunk] : make_uint4(0, 0, 0, 0);
+      const MxScale m = mx_scale(max_quad(amax_bits8(v)));
+      if (valid) {
+        q[chunk] = mx_quant8(v, m);
+        if (c == 0) e8m0[chunk / 4] = (uint8_t)m.code;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0, hipStream_t stream,
+                               int num_cus) {
+  constexpr int U = kMxU;
+  const uint64_t nchunks = n / 8;
+  const uint64_t full = nchunks / ((uint64_t)U * kWave);
+  uint64_t wgs = (full + 3) / 4;
+  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL((mx8_kernel<U>), dim3((uint32_t)wgs), dim3(256), 0, stream,
+                     static_cast<const uint4 *>(w), static_cast<uint2 *>(q),
+                     static_cast<uint8_t *>(e8m0), nchunks, full);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

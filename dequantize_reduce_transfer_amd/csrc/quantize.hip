@@ -1,0 +1,178 @@
+// quantize.hip -- block-128 FP8 quantize of a flat bf16 tensor on gfx950.
+//
+// Method ("FP8 Transmission Optimization for VLA Training", section "FP8
+// Transmission Optimization and Bottlenecks", Transmission Efficiency
+// bullet: FP8 e4m3/e5m2 wire format with blockwise scaling), per block of
+// 128 elements:
+//   amax = max |x|,  s = max(fl32(amax / FP8_MAX), 2^-126),
+//   q_i  = satRNE(fl32(x_i / s)).
+//
+// Mapping.  A block of 128 bf16 is 256 contiguous bytes = 16 lanes x 16 B, so
+// one wave-wide 16-byte load covers 4 blocks and every load instruction reads
+// 1 KiB contiguous.  A wave's tile is U such loads (U * 4 blocks), all issued
+// before any arithmetic.  The block amax is an integer max over sign-cleared
+// bf16 bits (packed u16 max inside the lane, then 4 DPP steps across the 16
+// lanes); no LDS is used.  Waves walk tiles grid-stride; the last wave also
+// handles the ragged tail (< one tile, possibly a partial block).
+//
+// The quotient without a per-element divide.  Per block: sp = s * f and
+// rp = RN(1 / sp) (one IEEE divide each), with f = 2^64 for blocks whose amax
+// is below 2^-60 (else 1) so that every residual below stays a normal number.
+// Per element, with x' = x * f (exact):
+//   q0 = RN(x' * rp);  e = RN(q0 * sp - x') (fma, exact);  q1 = RN(q0 - e * rp) (fma)
+// This is Markstein's correction; q1 equals RN(x / s) for every bf16 x and
+// fp32 s that can occur here (exhaustively checked on the host over all
+// significand pairs, including signed zeros).  q1 is then clamped to
+// +-FP8_MAX -- which cannot change an RNE result, since |x / s| exceeds
+// FP8_MAX by at most one fp32 rounding -- and converted by the hardware
+// packed FP8 conversion (round to nearest even).
+#include "fp8q_device.h"
+#include "launch.h"
+
+namespace fp8q {
+namespace {
+
+constexpr int kQuantU = 4;          // 1 KiB loads in flight per wave per tile
+constexpr int kWgPerCu = 8;         // 256-thread workgroups per CU in the grid
+
+struct BlockScale {
+  float s;        // the stored scale (NaN for a non-finite block)
+  float sp;       // s * f
+  float rp;       // RN(1 / sp)
+  float f;        // 2^64 for tiny blocks, else 1
+  bool finite;
+};
+
+template <int FMT>
+__device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
+  BlockScale b;
+  b.finite = amax_bits < 0x7F80u;
+  const float amax = __uint_as_float(amax_bits << 16);
+  float s = amax / fp8_max<FMT>();                 // IEEE fp32 divide
+  s = fmaxf(s, 0x1p-126f);
+  b.f = amax_bits < 0x2180u ? 0x1p64f : 1.0f;      // amax < 2^-60
+  b.sp = s * b.f;
+  b.rp = 1.0f / b.sp;                              // IEEE fp32 divide
+  b.s = b.finite ? s : __uint_as_float(0x7FC00000u);
+  return b;
+}
+
+template <int FMT>
+__device__ __forceinline__ float quotient(float x, const BlockScale &b) {
+  const float xp = x * b.f;
+  const float q0 = xp * b.rp;
+  const float e = __builtin_fmaf(q0, b.sp, -xp);
+  const float q1 = __builtin_fmaf(-e, b.rp, q0);
+  return __builtin_amdgcn_fmed3f(q1, -fp8_max<FMT>(), fp8_max<FMT>());
+}
+
+template <int FMT>
+__device__ __forceinline__ uint2 quant8(uint4 v, const BlockScale &b) {
+  uint2 r;
+  r.x = cvt4<FMT>(quotient<FMT>(bf16_lo(v.x), b), quotient<FMT>(bf16_hi(v.x), b),
+                  quotient<FMT>(bf16_lo(v.y), b), quotient<FMT>(bf16_hi(v.y), b));
+  r.y = cvt4<FMT>(quotient<FMT>(bf16_lo(v.z), b), quotient<FMT>(bf16_hi(v.z), b),
+                  quotient<FMT>(bf16_lo(v.w), b), quotient<FMT>(bf16_hi(v.w), b));
+  if (!b.finite) {
+    r.x = 0x7F7F7F7Fu;
+    r.y = 0x7F7F7F7Fu;
+  }
+  return r;
+}
+
+// The ragged end [start, n): whole blocks plus at most one partial block.
+// One wave, 4 blocks per pass (one per 16-lane row); elements past n read as
+// zero (which never raises an amax) and are never written.
+template <int FMT>
+__device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restrict__ q,
+                              float *__restrict__ scales, uint64_t n, uint64_t start) {
+  const uint32_t lane = lane_id();
+  const uint32_t row = lane >> 4, col = lane & 15;
+  for (uint64_t blk0 = start / kBlock; blk0 * kBlock < n; blk0 += 4) {
+    const uint64_t blk = blk0 + row;
+    const uint64_t e0 = blk * kBlock + col * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (e0 + 8 <= n) {
+      v = *reinterpret_cast<const uint4 *>(x + e0);
+    } else if (e0 < n) {
+      uint32_t h[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = (e0 + j < n) ? x[e0 + j] : 0u;
+      v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                     h[6] | (h[7] << 16));
+    }
+    const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v)));
+    const uint2 r = quant8<FMT>(v, b);
+    if (e0 + 8 <= n) {
+      *reinterpret_cast<uint2 *>(q + e0) = r;
+    } else if (e0 < n) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (e0 + j < n) q[e0 + j] = (uint8_t)((j < 4 ? r.x : r.y) >> (8 * (j & 3)));
+    }
+    if (col == 0 && blk * kBlock < n) scales[blk] = b.s;
+  }
+}
+
+template <int FMT, int U>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint4 *__restrict__ x,
+                                                       uint2 *__restrict__ q,
+                                                       float *__restrict__ scales, uint64_t n,
+                                                       uint64_t full_tiles) {
+  constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
+  constexpr uint64_t kBlocks = U * 4;              // blocks per tile
+  const uint32_t lane = lane_id();
+  const uint32_t row = lane >> 4, col = lane & 15;
+  const uint64_t nw = wave_count();
+  const uint64_t w0 = wave_index();
+
+  for (uint64_t t = w0; t < full_tiles; t += nw) {
+    const uint64_t c0 = t * kChunks;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = x[c0 + u * kWave + lane];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v[u])));
+      q[c0 + u * kWave + lane] = quant8<FMT>(v[u], b);
+      sc[u] = b.s;
+    }
+    // block (u, row) of the tile is block u * 4 + row; lane (row, col = u)
+    // stores it, so one instruction writes the tile's 16 scales (64 B).
+    if (col < U) {
+      float s = sc[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) s = (col == (uint32_t)u) ? sc[u] : s;
+      scales[t * kBlocks + col * 4 + row] = s;
+    }
+  }
+  if (w0 == nw - 1)
+    quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
+                       scales, n, full_tiles * kChunks * 8);
+}
+
+template <int FMT>
+hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream,
+                    int num_cus) {
+  constexpr int U = kQuantU;
+  const uint64_t tile_elems = (uint64_t)U * kWave * 8;
+  const uint64_t full = n / tile_elems;
+  uint64_t wgs = (full + 3) / 4;
+  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
+  if (wgs > cap) wgs = cap;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL((quantize_kernel<FMT, U>), dim3((uint32_t)wgs), dim3(256), 0, stream,
+                     static_cast<const uint4 *>(x), static_cast<uint2 *>(q), scales, n, full);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, const void *x, uint64_t n, void *q, float *scales,
+                           hipStream_t stream, int num_cus) {
+  return fmt == 0 ? launch_t<0>(x, n, q, scales, stream, num_cus)
+                  : launch_t<1>(x, n, q, scales, stream, num_cus);
+}
+
+}  // namespace fp8q

@@ -19,3 +19,13 @@ if TESTS not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: a longer CPU test (still minutes at most)")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr (uncaptured, flushed) before it runs, so a
+    run that dies on the GPU still says which case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write("\n[gpu case] %s\n" % request.node.nodeid)
+        sys.__stderr__.flush()
+    yield

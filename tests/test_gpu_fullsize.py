@@ -1,0 +1,112 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the same entry points on the same sizes).  Where the oracle
+cannot redo the whole output in seconds, sampled blocks / elements are
+checked exactly: every block (and every reduced element) depends only on its
+own inputs, so a sample is checked by running the oracle on just those
+inputs."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import dequantize_reduce_transfer_amd as fq
+import oracle
+from dequantize_reduce_transfer_amd import workloads
+from gpu_util import (assert_bf16_parity, assert_bytes_equal, assert_reduce_parity, f32_bits,
+                      host, require_gpu)
+from helpers import torch_fp8_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(nunits, count, seed, always=()):
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(min(64, nunits)), np.arange(max(0, nunits - 64), nunits),
+                          rng.integers(0, nunits, count), np.asarray(always, dtype=np.int64)])
+    return np.unique(idx[(idx >= 0) & (idx < nunits)])
+
+
+def test_pi05_gradient_quantize_e4m3_full():
+    """3.5e9-element bf16 gradient (~7 GB), one launch."""
+    dev = require_gpu()
+    n = workloads.PI05_N
+    x = workloads.segmented_gradient(n, seed=0, device=dev)
+    q, s = fq.fp8q_quantize(x, fq.E4M3)
+    torch.cuda.synchronize()
+    nb = n // 128
+    seg_edges = [(k * workloads.PI05_SEGMENT) // 128 for k in range(1, n // workloads.PI05_SEGMENT)]
+    idx = _sample(nb, 8192, seed=1, always=seg_edges)
+    it = torch.from_numpy(idx).to(dev)
+    xb = host(x.view(-1, 128)[it])
+    qb = host(q.view(-1, 128)[it])
+    sb = host(s[it])
+    q_o, s_o = oracle.quantize(xb.ravel(), fq.E4M3)
+    assert_bytes_equal(qb.ravel(), q_o, "pi05 sampled codes")
+    assert_bytes_equal(f32_bits(sb), f32_bits(s_o), "pi05 sampled scales")
+
+
+def test_pi05_reduce_k8_full():
+    """8 peer shards of 437,500,000 elements (3,417,969 blocks, 96-element tail) -> fp32."""
+    dev = require_gpu()
+    n, k = workloads.PI05_SHARD_N, workloads.PI05_PEERS
+    shards = [workloads.random_wire_shard(n, seed=200 + p, fmt=fq.E4M3, device=dev) for p in range(k)]
+    qs = [a for a, _ in shards]
+    ss = [b for _, b in shards]
+    y = fq.fp8q_dequant_reduce(qs, ss, fq.E4M3)
+    torch.cuda.synchronize()
+    idx = _sample(n, 16384, seed=2, always=np.arange(n - 300, n))
+    it = torch.from_numpy(idx).to(dev)
+    bt = torch.from_numpy(idx // 128).to(dev)
+    m = idx.size
+    # each sampled element becomes element 0 of its own 128-block
+    q_in, s_in = [], []
+    for q, s in zip(qs, ss):
+        qq = np.zeros((m, 128), np.uint8)
+        qq[:, 0] = host(q[it])
+        q_in.append(qq.ravel())
+        s_in.append(host(s[bt]))
+    want = oracle.dequant_reduce(q_in, s_in, fq.E4M3)[::128]
+    got = host(y[it])
+    mag = np.zeros(m)
+    for qq, s in zip(q_in, s_in):
+        mag += np.abs(torch_fp8_decode(qq[::128], fq.E4M3).astype(np.float64) * s)
+    assert_reduce_parity(got, want, mag, "pi05 reduce sampled")
+
+
+@pytest.mark.parametrize("name", ["gate", "up", "down"])
+def test_moe_layer_mx8_full(name):
+    """One Qwen3-30B-A3B-shaped MoE layer: 128 experts."""
+    dev = require_gpu()
+    experts, hidden, inter = workloads.MOE_EXPERTS, workloads.MOE_HIDDEN, workloads.MOE_INTER
+    shape = (experts, inter, hidden) if name != "down" else (experts, hidden, inter)
+    seed = {"gate": 0, "up": 1, "down": 2}[name]
+    w = workloads.kaiming_uniform(shape, seed, device=dev)
+    q, e = fq.mx8_quantize(w)
+    torch.cuda.synchronize()
+    K = shape[-1]
+    rows = w.numel() // K
+    assert tuple(e.shape) == (rows, K // 32)
+    idx = _sample(rows, 512, seed=3 + seed)
+    it = torch.from_numpy(idx).to(dev)
+    wr = host(w.view(rows, K)[it])
+    q_o, e_o = oracle.mx8_quantize(wr)
+    assert_bytes_equal(host(q.view(rows, K)[it]), q_o, name + " codes")
+    assert_bytes_equal(host(e[it]), e_o, name + " e8m0")
+
+
+@pytest.mark.parametrize("fmt", [fq.E4M3, fq.E5M2])
+def test_stress_full_payload_bf16(fmt):
+    """8 peers x 33,554,432 elements (64 MiB bf16 each), reduced into bf16."""
+    dev = require_gpu()
+    n = workloads.STRESS_N
+    bits = [workloads.bits(workloads.stress_payload(p, fmt, n=n, device=dev)) for p in range(8)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        shards = list(ex.map(lambda b: oracle.quantize(b, fmt), bits))
+    del bits
+    qs = [torch.from_numpy(a).to(dev) for a, _ in shards]
+    ss = [torch.from_numpy(b).to(dev) for _, b in shards]
+    y = fq.fp8q_dequant_reduce(qs, ss, fmt, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.dequant_reduce([a for a, _ in shards], [b for _, b in shards], fmt, out_bf16=True)
+    assert_bf16_parity(host(y), want, "stress full")

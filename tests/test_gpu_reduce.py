@@ -1,0 +1,182 @@
+"""GPU parity: dequantize and fused dequant-reduce (HIP, through the C ABI)
+against the oracle.  The reduce's gate is the 1e-6 relative bound on
+sum_p |d_p|; since both sides add the same products in the same order, the
+bits must match too."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import dequantize_reduce_transfer_amd as fq
+import oracle
+from dequantize_reduce_transfer_amd import workloads
+from gpu_util import (assert_bf16_parity, assert_bytes_equal, assert_reduce_parity, dev_f32,
+                      dev_u8, f32_bits, host, require_gpu)
+from helpers import torch_fp8_decode
+
+pytestmark = pytest.mark.gpu
+FMTS = [fq.E4M3, fq.E5M2]
+
+
+def _magnitudes(qs, ss, fmt):
+    """sum_p |dec(q_p) * s_p| in float64, for the relative gate."""
+    n = qs[0].size
+    m = np.zeros(n, np.float64)
+    for q, s in zip(qs, ss):
+        d = torch_fp8_decode(q, fmt).astype(np.float64) * np.repeat(s.astype(np.float64), 128)[:n]
+        m += np.abs(np.nan_to_num(d, nan=0.0, posinf=0.0, neginf=0.0))
+    return m
+
+
+def _oracle_shards(bits_list, fmt, workers=8):
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda b: oracle.quantize(b, fmt), bits_list))
+
+
+def _gpu_reduce(qs, ss, fmt, dev, out_dtype=torch.float32):
+    qd = [dev_u8(q, dev) for q in qs]
+    sd = [dev_f32(s, dev) for s in ss]
+    y = fq.fp8q_dequant_reduce(qd, sd, fmt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(y)
+
+
+def _check_reduce(qs, ss, fmt, dev, what):
+    y32 = _gpu_reduce(qs, ss, fmt, dev)
+    want32 = oracle.dequant_reduce(qs, ss, fmt)
+    assert_reduce_parity(y32, want32, _magnitudes(qs, ss, fmt), what + " f32")
+    ybf = _gpu_reduce(qs, ss, fmt, dev, torch.bfloat16)
+    assert_bf16_parity(ybf, oracle.dequant_reduce(qs, ss, fmt, out_bf16=True), what + " bf16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tiny_gradient_k4(fmt):
+    dev = require_gpu()
+    shards = _oracle_shards([workloads.bits(workloads.tiny_gradient(p)) for p in range(4)], fmt)
+    qs, ss = [a for a, _ in shards], [b for _, b in shards]
+    _check_reduce(qs, ss, fmt, dev, "tiny k=4")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequantize(fmt, out_dtype):
+    dev = require_gpu()
+    bits = workloads.bits(workloads.tiny_gradient(2))
+    q, s = oracle.quantize(bits, fmt)
+    y = fq.fp8q_dequantize(dev_u8(q, dev), dev_f32(s, dev), fmt, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    want = oracle.dequantize(q, s, fmt, out_bf16=(out_dtype == torch.bfloat16))
+    if out_dtype == torch.float32:
+        assert_bytes_equal(f32_bits(host(y)), f32_bits(want), "dequantize f32")
+    else:
+        assert_bf16_parity(host(y), want, "dequantize bf16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequantize_every_code_with_nan_scale(fmt):
+    dev = require_gpu()
+    q = np.tile(np.arange(256, dtype=np.uint8), 4)
+    s = np.array([1.0, 2.0 ** -126, np.nan, 3.0e30, 0.25, 7.0, 1e-20, 65536.0], np.float32)
+    y = host(fq.fp8q_dequantize(dev_u8(q, dev), dev_f32(s, dev), fmt))
+    want = oracle.dequantize(q, s, fmt)
+    assert np.array_equal(np.isnan(y), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert_bytes_equal(f32_bits(y[ok]), f32_bits(want[ok]), "every code")
+    yb = host(fq.fp8q_dequantize(dev_u8(q, dev), dev_f32(s, dev), fmt, out_dtype=torch.bfloat16))
+    assert_bf16_parity(yb, oracle.dequantize(q, s, fmt, out_bf16=True), "every code bf16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("k", list(range(1, 17)))
+def test_every_peer_count(fmt, k):
+    dev = require_gpu()
+    n = 128 * 300 + 77
+    shards = [workloads.random_wire_shard(n, seed=1000 * k + p, fmt=fmt) for p in range(k)]
+    qs = [a.numpy() for a, _ in shards]
+    ss = [b.numpy() for _, b in shards]
+    _check_reduce(qs, ss, fmt, dev, "k=%d" % k)
+
+
+@pytest.mark.parametrize("n", [1, 5, 127, 128, 255, 256, 257, 1023, 1024, 1025, 4096 + 100])
+def test_ragged_sizes_leave_canaries(n):
+    dev = require_gpu()
+    k = 3
+    shards = [workloads.random_wire_shard(n, seed=n + p, fmt=0) for p in range(k)]
+    qs = [dev_u8(a.numpy(), dev) for a, _ in shards]
+    ss = [dev_f32(b.numpy(), dev) for _, b in shards]
+    y_big = torch.full((n + 40,), -3.5, dtype=torch.float32, device=dev)
+    fq.fp8q_dequant_reduce(qs, ss, 0, out=y_big[:n])
+    yb_big = torch.full((n + 40,), 77, dtype=torch.int16, device=dev)
+    fq.fp8q_dequant_reduce(qs, ss, 0, out_dtype=torch.bfloat16, out=yb_big.view(torch.bfloat16)[:n])
+    torch.cuda.synchronize()
+    qh = [a.numpy() for a, _ in shards]
+    sh = [b.numpy() for _, b in shards]
+    yh = host(y_big)
+    assert_bytes_equal(f32_bits(yh[:n]), f32_bits(oracle.dequant_reduce(qh, sh, 0)), "n=%d" % n)
+    assert np.all(yh[n:] == -3.5)
+    ybh = host(yb_big)
+    assert_bf16_parity(ybh[:n].view(np.uint16), oracle.dequant_reduce(qh, sh, 0, out_bf16=True),
+                       "bf16 n=%d" % n)
+    assert np.all(ybh[n:] == 77)
+
+
+@pytest.mark.parametrize("nbytes", workloads.SWEEP_BYTES[:-1])
+def test_payload_sweep_e5m2_k8(nbytes):
+    dev = require_gpu()
+    bits = [workloads.bits(workloads.sweep_payload(nbytes, seed=p)) for p in range(8)]
+    shards = _oracle_shards(bits, fq.E5M2)
+    qs, ss = [a for a, _ in shards], [b for _, b in shards]
+    y = _gpu_reduce(qs, ss, fq.E5M2, dev)
+    assert_reduce_parity(y, oracle.dequant_reduce(qs, ss, fq.E5M2),
+                         _magnitudes(qs, ss, fq.E5M2), "sweep %d B" % nbytes)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_stress_share_bf16_out(fmt):
+    """One GPU's share of the 64 MiB stress payload: chunk 0 of 8 peers."""
+    dev = require_gpu()
+    n = workloads.STRESS_N // workloads.STRESS_CHUNKS
+    bits = [workloads.bits(workloads.stress_payload(p, fmt, n=n)) for p in range(8)]
+    shards = _oracle_shards(bits, fmt)
+    qs, ss = [a for a, _ in shards], [b for _, b in shards]
+    y = _gpu_reduce(qs, ss, fmt, dev, torch.bfloat16)
+    assert_bf16_parity(y, oracle.dequant_reduce(qs, ss, fmt, out_bf16=True), "stress share")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_naive_path_equals_fused(fmt):
+    dev = require_gpu()
+    n, k = 128 * 999 + 3, 8
+    shards = [workloads.random_wire_shard(n, seed=50 + p, fmt=fmt, device=dev) for p in range(k)]
+    qs = [a for a, _ in shards]
+    ss = [b for _, b in shards]
+    fused = fq.fp8q_dequant_reduce(qs, ss, fmt)
+    parts = [fq.fp8q_dequantize(q, s, fmt) for q, s in zip(qs, ss)]
+    naive = fq.fp8q_sum_f32(parts)
+    naive_bf = fq.fp8q_sum_f32(parts, out_dtype=torch.bfloat16)
+    fused_bf = fq.fp8q_dequant_reduce(qs, ss, fmt, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int32), naive.view(torch.int32))
+    assert torch.equal(fused_bf.view(torch.int16), naive_bf.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_peers_cancel_exactly(fmt):
+    dev = require_gpu()
+    bits = workloads.bits(workloads.tiny_gradient(4))
+    q0, s0 = oracle.quantize(bits, fmt)
+    q1, s1 = oracle.quantize(bits ^ 0x8000, fmt)
+    y = _gpu_reduce([q0, q1], [s0, s1], fmt, dev)
+    assert np.all(y == 0)
+
+
+def test_same_shard_twice_and_deterministic():
+    dev = require_gpu()
+    q, s = workloads.random_wire_shard(100_000, seed=9, fmt=0, device=dev)
+    a = fq.fp8q_dequant_reduce([q, q, q], [s, s, s], 0)
+    b = fq.fp8q_dequant_reduce([q, q, q], [s, s, s], 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    want = oracle.dequant_reduce([host(q)] * 3, [host(s)] * 3, 0)
+    assert_bytes_equal(f32_bits(host(a)), f32_bits(want), "same shard x3")

@@ -8,7 +8,6 @@
 // prequantized-refit handshake does in "perf: Reduce MXFP8 refit
 // weight-transfer overheads", section "Safety").  The library never
 // allocates device memory: every buffer is the caller's.
-#include <atomic>
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -17,9 +16,6 @@
 #include "launch.h"
 
 namespace {
-
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_num_cus[kMaxDevices];
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -35,25 +31,6 @@ size_t num_blocks(size_t n, size_t block) { return (n + block - 1) / block; }
 bool valid_fmt(fp8q_format f) { return f == FP8Q_E4M3 || f == FP8Q_E5M2; }
 bool valid_out(fp8q_out_dtype d) { return d == FP8Q_OUT_F32 || d == FP8Q_OUT_BF16; }
 size_t out_elem_bytes(fp8q_out_dtype d) { return d == FP8Q_OUT_F32 ? 4 : 2; }
-
-// Compute units of the current device, queried once per device.
-fp8q_status device_cus(int *cus) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FP8Q_ERR_HIP;
-  if (dev >= 0 && dev < kMaxDevices) {
-    int c = g_num_cus[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *cus = c;
-      return FP8Q_OK;
-    }
-  }
-  int c = 0;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-    return FP8Q_ERR_HIP;
-  if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(c, std::memory_order_relaxed);
-  *cus = c;
-  return FP8Q_OK;
-}
 
 fp8q_status from_hip(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_HIP; }
 
@@ -72,11 +49,8 @@ fp8q_status fp8q_quantize(const void *x_bf16, size_t n, fp8q_format fmt, void *q
   if (overlaps(x_bf16, 2 * n, q_out, n) || overlaps(x_bf16, 2 * n, scales_out, sb) ||
       overlaps(q_out, n, scales_out, sb))
     return FP8Q_ERR_OVERLAP;
-  int cus = 0;
-  fp8q_status st = device_cus(&cus);
-  if (st != FP8Q_OK) return st;
   return from_hip(fp8q::launch_quantize((int)fmt, x_bf16, n, q_out, scales_out,
-                                        static_cast<hipStream_t>(stream), cus));
+                                        static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status fp8q_dequant_reduce(const void *const *q_peers, const float *const *scales_peers, int k,
@@ -97,12 +71,9 @@ fp8q_status fp8q_dequant_reduce(const void *const *q_peers, const float *const *
   for (int p = 0; p < k; ++p)
     if (overlaps(y_out, yb, q_peers[p], n) || overlaps(y_out, yb, scales_peers[p], sb))
       return FP8Q_ERR_OVERLAP;
-  int cus = 0;
-  fp8q_status st = device_cus(&cus);
-  if (st != FP8Q_OK) return st;
   return from_hip(fp8q::launch_dequant_reduce((int)fmt, k, out_dtype == FP8Q_OUT_BF16, q_peers,
                                               scales_peers, n, y_out,
-                                              static_cast<hipStream_t>(stream), cus));
+                                              static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status fp8q_dequantize(const void *q, const float *scales, size_t n, fp8q_format fmt,
@@ -128,11 +99,8 @@ fp8q_status mx8_quantize(const void *w_bf16, size_t rows, size_t K, void *q_out,
   if (overlaps(w_bf16, 2 * n, q_out, n) || overlaps(w_bf16, 2 * n, e8m0_out, eb) ||
       overlaps(q_out, n, e8m0_out, eb))
     return FP8Q_ERR_OVERLAP;
-  int cus = 0;
-  fp8q_status st = device_cus(&cus);
-  if (st != FP8Q_OK) return st;
   return from_hip(fp8q::launch_mx8_quantize(w_bf16, n, q_out, e8m0_out,
-                                            static_cast<hipStream_t>(stream), cus));
+                                            static_cast<hipStream_t>(stream)));
 }
 
 fp8q_status fp8q_sum_f32(const float *const *parts, int k, size_t n, void *y_out,
@@ -150,11 +118,8 @@ fp8q_status fp8q_sum_f32(const float *const *parts, int k, size_t n, void *y_out
   const size_t yb = out_elem_bytes(out_dtype) * n;
   for (int p = 0; p < k; ++p)
     if (overlaps(y_out, yb, parts[p], 4 * n)) return FP8Q_ERR_OVERLAP;
-  int cus = 0;
-  fp8q_status st = device_cus(&cus);
-  if (st != FP8Q_OK) return st;
   return from_hip(fp8q::launch_sum_f32(k, out_dtype == FP8Q_OUT_BF16, parts, n, y_out,
-                                       static_cast<hipStream_t>(stream), cus));
+                                       static_cast<hipStream_t>(stream)));
 }
 
 const char *fp8q_status_str(fp8q_status s) {

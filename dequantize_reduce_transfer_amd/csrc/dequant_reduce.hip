@@ -27,7 +27,15 @@
 namespace fp8q {
 namespace {
 
-constexpr int kWgPerCu = 8;
+#ifndef FP8Q_RED_U4
+#define FP8Q_RED_U4 4        // tile depth for k <= 4
+#endif
+#ifndef FP8Q_RED_U8
+#define FP8Q_RED_U8 2        // tile depth for 4 < k <= 8
+#endif
+#ifndef FP8Q_RED_U16
+#define FP8Q_RED_U16 1       // tile depth for 8 < k <= 16
+#endif
 
 struct PeerPtrs {
   const uint32_t *q[kMaxPeers];
@@ -42,16 +50,21 @@ struct PartPtrs {
 // 2U scales of every peer fit the scalar register file.
 template <int K>
 constexpr int reduce_u() {
-  return K <= 4 ? 4 : (K <= 8 ? 2 : 1);
+  return K <= 4 ? FP8Q_RED_U4 : (K <= 8 ? FP8Q_RED_U8 : FP8Q_RED_U16);
 }
+
+// Non-temporal code loads pay off when several peers stream in; the single
+// shard of a dequantize measured faster with ordinary loads.
+template <int K>
+constexpr bool kNtCodes = (FP8Q_NT_LOAD != 0) && K > 1;
 
 template <bool BF16>
 __device__ __forceinline__ void store4(void *y, uint64_t elem, float a, float b, float c, float d) {
   if constexpr (BF16) {
-    uint2 r = make_uint2(bf16_pack2(a, b), bf16_pack2(c, d));
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(y) + elem) = r;
+    st(reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(y) + elem),
+       u32x2{bf16_pack2(a, b), bf16_pack2(c, d)});
   } else {
-    *reinterpret_cast<float4 *>(static_cast<float *>(y) + elem) = make_float4(a, b, c, d);
+    st(reinterpret_cast<f32x4 *>(static_cast<float *>(y) + elem), f32x4{a, b, c, d});
   }
 }
 
@@ -103,7 +116,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
 #pragma unroll
     for (int p = 0; p < K; ++p)
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[p][u] = P.q[p][dw0 + u * kWave + lane];
+      for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
 
     float acc[U][4];
 #pragma unroll
@@ -132,28 +145,22 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
 }
 
 template <int FMT, int K, bool BF16>
-hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream,
-                           int num_cus) {
+hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = reduce_u<K>();
   const uint64_t tile = (uint64_t)U * 256;
   const uint64_t full = n / tile;
-  uint64_t wgs = (full + 3) / 4;
-  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
-  if (wgs > cap) wgs = cap;
-  if (wgs < 1) wgs = 1;
-  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, BF16>), dim3((uint32_t)wgs), dim3(256), 0, stream,
-                     P, y, n, full);
+  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, BF16>), dim3(grid_for_tiles(full)), dim3(256), 0,
+                     stream, P, y, n, full);
   return hipGetLastError();
 }
 
 template <int FMT, bool BF16, int K = 1>
-hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream,
-                      int num_cus) {
+hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   if constexpr (K > kMaxPeers) {
     return hipErrorInvalidValue;
   } else {
-    if (k == K) return launch_reduce_t<FMT, K, BF16>(P, n, y, stream, num_cus);
-    return dispatch_k<FMT, BF16, K + 1>(k, P, n, y, stream, num_cus);
+    if (k == K) return launch_reduce_t<FMT, K, BF16>(P, n, y, stream);
+    return dispatch_k<FMT, BF16, K + 1>(k, P, n, y, stream);
   }
 }
 
@@ -185,31 +192,29 @@ __global__ __launch_bounds__(256) void sum_kernel(PartPtrs P, int k, void *__res
 
 hipError_t launch_dequant_reduce(int fmt, int k, bool out_bf16, const void *const *q,
                                  const float *const *scales, uint64_t n, void *y,
-                                 hipStream_t stream, int num_cus) {
+                                 hipStream_t stream) {
   PeerPtrs P = {};
   for (int p = 0; p < k; ++p) {
     P.q[p] = static_cast<const uint32_t *>(q[p]);
     P.s[p] = scales[p];
   }
   if (fmt == 0)
-    return out_bf16 ? dispatch_k<0, true>(k, P, n, y, stream, num_cus)
-                    : dispatch_k<0, false>(k, P, n, y, stream, num_cus);
-  return out_bf16 ? dispatch_k<1, true>(k, P, n, y, stream, num_cus)
-                  : dispatch_k<1, false>(k, P, n, y, stream, num_cus);
+    return out_bf16 ? dispatch_k<0, true>(k, P, n, y, stream)
+                    : dispatch_k<0, false>(k, P, n, y, stream);
+  return out_bf16 ? dispatch_k<1, true>(k, P, n, y, stream)
+                  : dispatch_k<1, false>(k, P, n, y, stream);
 }
 
 hipError_t launch_sum_f32(int k, bool out_bf16, const float *const *parts, uint64_t n, void *y,
-                          hipStream_t stream, int num_cus) {
+                          hipStream_t stream) {
   PartPtrs P = {};
   for (int p = 0; p < k; ++p) P.p[p] = parts[p];
-  uint64_t wgs = (n / 4 + 255) / 256;
-  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
-  if (wgs > cap) wgs = cap;
-  if (wgs < 1) wgs = 1;
+  // one float4 per thread: 256 threads = 4 "tiles" of 64 float4
+  const uint32_t wgs = grid_for_tiles((n / 4 + 63) / 64);
   if (out_bf16)
-    hipLaunchKernelGGL(sum_kernel<true>, dim3((uint32_t)wgs), dim3(256), 0, stream, P, k, y, n);
+    hipLaunchKernelGGL(sum_kernel<true>, dim3(wgs), dim3(256), 0, stream, P, k, y, n);
   else
-    hipLaunchKernelGGL(sum_kernel<false>, dim3((uint32_t)wgs), dim3(256), 0, stream, P, k, y, n);
+    hipLaunchKernelGGL(sum_kernel<false>, dim3(wgs), dim3(256), 0, stream, P, k, y, n);
   return hipGetLastError();
 }
 

@@ -8,7 +8,38 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Streaming hints: non-temporal loads / stores (global_load/store ... nt).
+// Every byte is touched once, so keeping it out of the caches measured
+// 3-10% faster on the streaming kernels.
+#ifndef FP8Q_NT_LOAD
+#define FP8Q_NT_LOAD 1
+#endif
+#ifndef FP8Q_NT_STORE
+#define FP8Q_NT_STORE 1
+#endif
+
 namespace fp8q {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, bool NT = (FP8Q_NT_LOAD != 0)>
+__device__ __forceinline__ T ld(const T *p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T *p, T v) {
+#if FP8Q_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 
 constexpr int kWave = 64;
 constexpr int kBlock = 128;      // elements per fp32 scale
@@ -41,10 +72,10 @@ __device__ __forceinline__ uint32_t max_row16(uint32_t v) {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// Largest sign-cleared bf16 bit pattern among the 8 bf16 held in a uint4.
+// Largest sign-cleared bf16 bit pattern among the 8 bf16 held in a u32x4.
 // For finite values this is the bit pattern of max |x|; inf / NaN patterns
 // (>= 0x7F80) order above every finite one.
-__device__ __forceinline__ uint32_t amax_bits8(uint4 v) {
+__device__ __forceinline__ uint32_t amax_bits8(u32x4 v) {
   const uint32_t m = 0x7FFF7FFFu;
   u16x2 a = __builtin_bit_cast(u16x2, v.x & m);
   u16x2 b = __builtin_bit_cast(u16x2, v.y & m);

@@ -3,6 +3,10 @@
 // Each launcher assumes the arguments were validated by the C-ABI layer
 // (non-null, aligned, non-overlapping, 0 < n <= FP8Q_MAX_ELEMS) and only
 // sizes the grid and enqueues the kernel on `stream`.
+//
+// Tuning constants (tile depths, streaming hints) are compile-time macros
+// with the defaults chosen by measurement on MI355X at the full workload
+// sizes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,21 +16,35 @@ namespace fp8q {
 
 constexpr int kMaxPeers = 16;
 
+// Grid size: one 4-wave workgroup per 4 tiles, so that the tiles in flight
+// at any moment form one contiguous window of the buffer (measured faster on
+// MI355X than a persistent grid, whose waves drift apart across the whole
+// buffer).  The cap keeps grid * 256 work-items inside the dispatch packet's
+// 32-bit range; beyond it the kernels' grid-stride loops take the rest.
+constexpr uint64_t kMaxWorkgroups = 1ull << 22;
+
+inline uint32_t grid_for_tiles(uint64_t tiles) {
+  uint64_t wgs = (tiles + 3) / 4;
+  if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
+  if (wgs < 1) wgs = 1;
+  return (uint32_t)wgs;
+}
+
 // Block-128 quantize of n bf16 values (fmt 0 = E4M3, 1 = E5M2).
 hipError_t launch_quantize(int fmt, const void *x, uint64_t n, void *q, float *scales,
-                           hipStream_t stream, int num_cus);
+                           hipStream_t stream);
 
 // Fused dequantize-then-reduce of k shards (k == 1 is a dequantize).
 hipError_t launch_dequant_reduce(int fmt, int k, bool out_bf16, const void *const *q,
                                  const float *const *scales, uint64_t n, void *y,
-                                 hipStream_t stream, int num_cus);
+                                 hipStream_t stream);
 
 // Ordered sum of k fp32 arrays (the naive path's reduction).
 hipError_t launch_sum_f32(int k, bool out_bf16, const float *const *parts, uint64_t n, void *y,
-                          hipStream_t stream, int num_cus);
+                          hipStream_t stream);
 
 // MXFP8 quantize of n bf16 values laid out as [rows, K] with K % 32 == 0.
 hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0,
-                               hipStream_t stream, int num_cus);
+                               hipStream_t stream);
 
 }  // namespace fp8q

@@ -29,8 +29,11 @@
 namespace fp8q {
 namespace {
 
-constexpr int kMxU = 4;            // 1 KiB loads in flight per wave per tile (<= 4)
-constexpr int kWgPerCu = 8;
+#ifndef FP8Q_MX_U
+#define FP8Q_MX_U 2
+#endif
+constexpr int kMxU = FP8Q_MX_U;              // 1 KiB loads in flight per wave per tile (<= 4)
+static_assert(kMxU >= 1 && kMxU <= 4, "one E8M0 byte per lane covers at most 4 loads");
 
 struct MxScale {
   uint32_t code;   // E8M0 byte
@@ -52,8 +55,8 @@ __device__ __forceinline__ float mx_q(float x, float mul) {
   return __builtin_amdgcn_fmed3f(x * mul, -448.0f, 448.0f);
 }
 
-__device__ __forceinline__ uint2 mx_quant8(uint4 v, const MxScale &m) {
-  uint2 r;
+__device__ __forceinline__ u32x2 mx_quant8(u32x4 v, const MxScale &m) {
+  u32x2 r;
   r.x = cvt4<0>(mx_q(bf16_lo(v.x), m.mul), mx_q(bf16_hi(v.x), m.mul), mx_q(bf16_lo(v.y), m.mul),
                 mx_q(bf16_hi(v.y), m.mul));
   r.y = cvt4<0>(mx_q(bf16_lo(v.z), m.mul), mx_q(bf16_hi(v.z), m.mul), mx_q(bf16_lo(v.w), m.mul),
@@ -66,7 +69,7 @@ __device__ __forceinline__ uint2 mx_quant8(uint4 v, const MxScale &m) {
 }
 
 template <int U>
-__global__ __launch_bounds__(256) void mx8_kernel(const uint4 *__restrict__ w, uint2 *__restrict__ q,
+__global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u32x2 *__restrict__ q,
                                                   uint8_t *__restrict__ e8m0, uint64_t nchunks,
                                                   uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
@@ -78,14 +81,14 @@ __global__ __launch_bounds__(256) void mx8_kernel(const uint4 *__restrict__ w, u
 
   for (uint64_t t = w0; t < full_tiles; t += nw) {
     const uint64_t c0 = t * kChunks;
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = w[c0 + u * kWave + lane];
+    for (int u = 0; u < U; ++u) v[u] = ld(w + c0 + u * kWave + lane);
     uint32_t codes[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const MxScale m = mx_scale(max_quad(amax_bits8(v[u])));
-      q[c0 + u * kWave + lane] = mx_quant8(v[u], m);
+      st(q + c0 + u * kWave + lane, mx_quant8(v[u], m));
       codes[u] = m.code;
     }
     if (c < U) {
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void mx8_kernel(const uint4 *__restrict__ w, u
     for (uint64_t base = full_tiles * kChunks; base < nchunks; base += kWave) {
       const uint64_t chunk = base + lane;
       const bool valid = chunk < nchunks;
-      const uint4 v = valid ? w[chunk] : make_uint4(0, 0, 0, 0);
+      const u32x4 v = valid ? w[chunk] : u32x4{0u, 0u, 0u, 0u};
       const MxScale m = mx_scale(max_quad(amax_bits8(v)));
       if (valid) {
         q[chunk] = mx_quant8(v, m);
@@ -113,17 +116,13 @@ __global__ __launch_bounds__(256) void mx8_kernel(const uint4 *__restrict__ w, u
 
 }  // namespace
 
-hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0, hipStream_t stream,
-                               int num_cus) {
+hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0,
+                               hipStream_t stream) {
   constexpr int U = kMxU;
   const uint64_t nchunks = n / 8;
   const uint64_t full = nchunks / ((uint64_t)U * kWave);
-  uint64_t wgs = (full + 3) / 4;
-  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
-  if (wgs > cap) wgs = cap;
-  if (wgs < 1) wgs = 1;
-  hipLaunchKernelGGL((mx8_kernel<U>), dim3((uint32_t)wgs), dim3(256), 0, stream,
-                     static_cast<const uint4 *>(w), static_cast<uint2 *>(q),
+  hipLaunchKernelGGL((mx8_kernel<U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,
+                     static_cast<const u32x4 *>(w), static_cast<u32x2 *>(q),
                      static_cast<uint8_t *>(e8m0), nchunks, full);
   return hipGetLastError();
 }

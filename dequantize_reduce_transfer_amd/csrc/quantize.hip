@@ -12,8 +12,10 @@
 // 1 KiB contiguous.  A wave's tile is U such loads (U * 4 blocks), all issued
 // before any arithmetic.  The block amax is an integer max over sign-cleared
 // bf16 bits (packed u16 max inside the lane, then 4 DPP steps across the 16
-// lanes); no LDS is used.  Waves walk tiles grid-stride; the last wave also
-// handles the ragged tail (< one tile, possibly a partial block).
+// lanes); no LDS is used.  The grid has one wave per tile (grid-stride only
+// past the dispatch limit); the last wave also handles the ragged tail
+// (< one tile, possibly a partial block).  Loads and stores are
+// non-temporal: every byte is touched once.
 //
 // The quotient without a per-element divide.  Per block: sp = s * f and
 // rp = RN(1 / sp) (one IEEE divide each), with f = 2^64 for blocks whose amax
@@ -32,8 +34,10 @@
 namespace fp8q {
 namespace {
 
-constexpr int kQuantU = 4;          // 1 KiB loads in flight per wave per tile
-constexpr int kWgPerCu = 8;         // 256-thread workgroups per CU in the grid
+#ifndef FP8Q_QUANT_U
+#define FP8Q_QUANT_U 4
+#endif
+constexpr int kQuantU = FP8Q_QUANT_U;            // 1 KiB loads in flight per wave per tile
 
 struct BlockScale {
   float s;        // the stored scale (NaN for a non-finite block)
@@ -67,8 +71,8 @@ __device__ __forceinline__ float quotient(float x, const BlockScale &b) {
 }
 
 template <int FMT>
-__device__ __forceinline__ uint2 quant8(uint4 v, const BlockScale &b) {
-  uint2 r;
+__device__ __forceinline__ u32x2 quant8(u32x4 v, const BlockScale &b) {
+  u32x2 r;
   r.x = cvt4<FMT>(quotient<FMT>(bf16_lo(v.x), b), quotient<FMT>(bf16_hi(v.x), b),
                   quotient<FMT>(bf16_lo(v.y), b), quotient<FMT>(bf16_hi(v.y), b));
   r.y = cvt4<FMT>(quotient<FMT>(bf16_lo(v.z), b), quotient<FMT>(bf16_hi(v.z), b),
@@ -91,20 +95,20 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
   for (uint64_t blk0 = start / kBlock; blk0 * kBlock < n; blk0 += 4) {
     const uint64_t blk = blk0 + row;
     const uint64_t e0 = blk * kBlock + col * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
+    u32x4 v = {0u, 0u, 0u, 0u};
     if (e0 + 8 <= n) {
-      v = *reinterpret_cast<const uint4 *>(x + e0);
+      v = *reinterpret_cast<const u32x4 *>(x + e0);
     } else if (e0 < n) {
       uint32_t h[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) h[j] = (e0 + j < n) ? x[e0 + j] : 0u;
-      v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                     h[6] | (h[7] << 16));
+      v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                h[6] | (h[7] << 16)};
     }
     const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v)));
-    const uint2 r = quant8<FMT>(v, b);
+    const u32x2 r = quant8<FMT>(v, b);
     if (e0 + 8 <= n) {
-      *reinterpret_cast<uint2 *>(q + e0) = r;
+      *reinterpret_cast<u32x2 *>(q + e0) = r;
     } else if (e0 < n) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -115,8 +119,8 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 }
 
 template <int FMT, int U>
-__global__ __launch_bounds__(256) void quantize_kernel(const uint4 *__restrict__ x,
-                                                       uint2 *__restrict__ q,
+__global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__ x,
+                                                       u32x2 *__restrict__ q,
                                                        float *__restrict__ scales, uint64_t n,
                                                        uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
@@ -128,14 +132,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4 *__restrict__
 
   for (uint64_t t = w0; t < full_tiles; t += nw) {
     const uint64_t c0 = t * kChunks;
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = x[c0 + u * kWave + lane];
+    for (int u = 0; u < U; ++u) v[u] = ld(x + c0 + u * kWave + lane);
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v[u])));
-      q[c0 + u * kWave + lane] = quant8<FMT>(v[u], b);
+      st(q + c0 + u * kWave + lane, quant8<FMT>(v[u], b));
       sc[u] = b.s;
     }
     // block (u, row) of the tile is block u * 4 + row; lane (row, col = u)
@@ -153,26 +157,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint4 *__restrict__
 }
 
 template <int FMT>
-hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream,
-                    int num_cus) {
+hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
   constexpr int U = kQuantU;
   const uint64_t tile_elems = (uint64_t)U * kWave * 8;
   const uint64_t full = n / tile_elems;
-  uint64_t wgs = (full + 3) / 4;
-  const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * kWgPerCu;
-  if (wgs > cap) wgs = cap;
-  if (wgs < 1) wgs = 1;
-  hipLaunchKernelGGL((quantize_kernel<FMT, U>), dim3((uint32_t)wgs), dim3(256), 0, stream,
-                     static_cast<const uint4 *>(x), static_cast<uint2 *>(q), scales, n, full);
+  hipLaunchKernelGGL((quantize_kernel<FMT, U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,
+                     static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, full);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quantize(int fmt, const void *x, uint64_t n, void *q, float *scales,
-                           hipStream_t stream, int num_cus) {
-  return fmt == 0 ? launch_t<0>(x, n, q, scales, stream, num_cus)
-                  : launch_t<1>(x, n, q, scales, stream, num_cus);
+                           hipStream_t stream) {
+  return fmt == 0 ? launch_t<0>(x, n, q, scales, stream) : launch_t<1>(x, n, q, scales, stream);
 }
 
 }  // namespace fp8q

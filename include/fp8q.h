@@ -23,8 +23,7 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued on it and the call returns without synchronising.
  *   - The caller owns every buffer.  The library allocates no device memory,
- *     keeps no pointer after returning and holds no mutable global state
- *     other than a per-device cache of the compute-unit count.
+ *     keeps no pointer after returning and holds no mutable global state.
  *   - Every argument is checked on the host before anything is launched.  On
  *     any error the call returns a non-zero status, launches nothing and
  *     writes no output byte.  n == 0 (or rows * K == 0) is a successful no-op.

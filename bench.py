@@ -139,6 +139,102 @@ def cpu_baseline(x, peers, moe, frac, fmt):
     }
 
 
+def median_ms(torch, fns):
+    """Median HIP-event time of a list of launches (one event pair each)."""
+    ts = []
+    for fn in fns:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    v = sorted(a.elapsed_time(b) for a, b in ts)
+    return v[len(v) // 2]
+
+
+def payload_sweep(torch, fq, workloads, dev, reps=20):
+    """e5m2 block quantize and k = 8 fused reduce (fp32 out) at the payload
+    sizes of the sweep, each launch on a different window of 2 GiB pools so
+    that the timed bytes come from HBM, not the 256 MB Infinity Cache."""
+    n_pool = 1 << 30
+    x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)
+    q = torch.empty(n_pool, dtype=torch.uint8, device=dev)
+    s = torch.empty(n_pool // 128, dtype=torch.float32, device=dev)
+    fq.fp8q_quantize(x, fq.E5M2, q_out=q, scales_out=s)
+    y = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    out = []
+    for nbytes in workloads.SWEEP_BYTES:
+        n = nbytes // 2
+        span = (n_pool - 9 * n) // 128 * 128
+
+        def off(i):
+            return (i * 9 * n) % span // 128 * 128
+
+        def quant(i):
+            o = off(i)
+            return lambda: fq.fp8q_quantize(x[o:o + n], fq.E5M2, q_out=q[o:o + n],
+                                            scales_out=s[o // 128:o // 128 + fq.num_scales(n)])
+
+        def red(i):
+            o = off(i)
+            qs = [q[o + p * n:o + (p + 1) * n] for p in range(8)]
+            ss = [s[(o + p * n) // 128:(o + p * n) // 128 + fq.num_scales(n)] for p in range(8)]
+            yo = (i * n) % ((1 << 28) - n) // 4 * 4
+            return lambda: fq.fp8q_dequant_reduce(qs, ss, fq.E5M2, out=y[yo:yo + n])
+
+        for fn in [quant(i) for i in range(3)] + [red(i) for i in range(3)]:
+            fn()
+        qm = median_ms(torch, [quant(i) for i in range(reps)])
+        rm = median_ms(torch, [red(i) for i in range(reps)])
+        out.append({"payload_bytes": nbytes, "elements": n,
+                    "quantize_us": round(qm * 1e3, 2),
+                    "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
+                    "quantize_bf16_equiv_GBps": round(2 * n / qm / 1e6, 1),
+                    "reduce_k8_us": round(rm * 1e3, 2),
+                    "reduce_k8_hbm_GBps": round(reduce_bytes_per_elem(8, 4) * n / rm / 1e6, 1),
+                    "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1)})
+    del x, q, s, y
+    return out
+
+
+def stress_reduce(torch, fq, workloads, dev, reps=20):
+    """k = 8 fused reduce into bf16 over the stress payload's shape: 8 peers x
+    33,554,432 elements in 8 all-to-all chunks; "share" is one chunk (one
+    GPU's part), "full" is all of it.  The reduce's time does not depend on
+    the code values, so the shards are drawn directly as wire codes."""
+    n, chunks = workloads.STRESS_N, workloads.STRESS_CHUNKS
+    res = {}
+    for fmt, name in ((fq.E4M3, "e4m3"), (fq.E5M2, "e5m2")):
+        shards = [workloads.random_wire_shard(n, seed=300 + p, fmt=fmt, device=dev) for p in range(8)]
+        y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        c = n // chunks
+
+        def share(i):
+            j = i % chunks
+            qs = [a[j * c:(j + 1) * c] for a, _ in shards]
+            ss = [b[j * c // 128:(j + 1) * c // 128] for _, b in shards]
+            return lambda: fq.fp8q_dequant_reduce(qs, ss, fmt, out_dtype=torch.bfloat16,
+                                                  out=y[j * c:(j + 1) * c])
+
+        full = lambda: fq.fp8q_dequant_reduce([a for a, _ in shards], [b for _, b in shards], fmt,
+                                              out_dtype=torch.bfloat16, out=y)
+        for i in range(3):
+            share(i)()
+            full()
+        sm = median_ms(torch, [share(i) for i in range(reps)])
+        fm = median_ms(torch, [full for _ in range(reps)])
+        alg = reduce_bytes_per_elem(8, 2)
+        res[name] = {"share_elements": c, "share_us": round(sm * 1e3, 2),
+                     "share_hbm_GBps": round(alg * c / sm / 1e6, 1),
+                     "full_elements": n, "full_us": round(fm * 1e3, 2),
+                     "full_hbm_GBps": round(alg * n / fm / 1e6, 1),
+                     "full_frac_peak": round(alg * n / fm / 1e6 / HBM_PEAK_GBS, 4)}
+        del shards, y
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +369,9 @@ def main():
         side["naive_dequant_then_sum_k8_us"] = round(naive_ms * 1e3, 2)
         side["fused_speedup_vs_naive"] = round(naive_ms / r_ms, 2)
         del parts
+        log("side figures: payload sweep (e5m2) and stress reduce (bf16 out)")
+        side["payload_sweep_e5m2"] = payload_sweep(torch, fq, workloads, dev)
+        side["stress_reduce_k8_bf16"] = stress_reduce(torch, fq, workloads, dev)
 
     roofline = {
         "bound": "hbm",

@@ -68,6 +68,10 @@ def _load():
     lib.oracle_mx8_quantize.restype = I
     lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e8m0_decode.restype = ctypes.c_float
+    lib.oracle_quantize_tensorwise.argtypes = [P, S, I, P, P]
+    lib.oracle_reduce_requantize.argtypes = [P, P, I, S, I, I, P, P]
+    lib.oracle_mx8_dequant_reduce.argtypes = [P, P, I, S, S, P, I]
+    lib.oracle_mx8_dequant_reduce.restype = I
     _lib = lib
     return lib
 
@@ -176,3 +180,60 @@ def mx8_quantize(w_bits):
         if rc != 0:
             raise ValueError("oracle rejected K")
     return q, e
+
+
+def quantize_tensorwise(x_bits, fmt: int):
+    """One fp32 scale for the whole tensor -> (q uint8[n], scale f32[1])."""
+    x = _c(x_bits, np.uint16).reshape(-1)
+    q = np.empty(x.size, dtype=np.uint8)
+    s = np.empty(1, dtype=np.float32)
+    if x.size == 0:
+        s[0] = 2.0 ** -126
+        return q, s
+    _load().oracle_quantize_tensorwise(_ptr(x), x.size, fmt, _ptr(q), _ptr(s))
+    return q, s
+
+
+def reduce_requantize(qs, ss, fmt_in: int, fmt_out: int):
+    """Dequant-reduce k shards, then block-128 quantize the fp32 sums."""
+    k = len(qs)
+    if k < 1 or k != len(ss):
+        raise ValueError("need k >= 1 shards with one scale array each")
+    qs = [_c(q, np.uint8).reshape(-1) for q in qs]
+    ss = [_c(s, np.float32).reshape(-1) for s in ss]
+    n = qs[0].size
+    for q, s in zip(qs, ss):
+        if q.size != n or s.size < num_blocks(n):
+            raise ValueError("shard shape mismatch")
+    qp = (ctypes.c_void_p * k)(*[_ptr(q) for q in qs])
+    sp = (ctypes.c_void_p * k)(*[_ptr(s) for s in ss])
+    q_out = np.empty(n, dtype=np.uint8)
+    s_out = np.empty(num_blocks(n), dtype=np.float32)
+    if n:
+        _load().oracle_reduce_requantize(qp, sp, k, n, fmt_in, fmt_out, _ptr(q_out), _ptr(s_out))
+    return q_out, s_out
+
+
+def mx8_dequant_reduce(qs, es, out_bf16: bool = False) -> np.ndarray:
+    """Ordered fp32 sum over k MXFP8 shards (q [rows, K], e8m0 [rows, K/32])."""
+    k = len(qs)
+    if k < 1 or k != len(es):
+        raise ValueError("need k >= 1 shards with one scale array each")
+    qs = [_c(q, np.uint8) for q in qs]
+    es = [_c(e, np.uint8) for e in es]
+    K = qs[0].shape[-1]
+    rows = qs[0].size // K if K else 0
+    for q, e in zip(qs, es):
+        if q.shape != qs[0].shape or e.size != rows * (K // MX_BLOCK):
+            raise ValueError("shard shape mismatch")
+    qp = (ctypes.c_void_p * k)(*[_ptr(q) for q in qs])
+    ep = (ctypes.c_void_p * k)(*[_ptr(e) for e in es])
+    y = np.empty(qs[0].shape, dtype=np.uint16 if out_bf16 else np.float32)
+    if qs[0].size:
+        if _load().oracle_mx8_dequant_reduce(qp, ep, k, rows, K, _ptr(y), int(out_bf16)) != 0:
+            raise ValueError("K must be a multiple of 32")
+    return y
+
+
+def mx8_dequantize(q, e8m0, out_bf16: bool = False) -> np.ndarray:
+    return mx8_dequant_reduce([q], [e8m0], out_bf16)

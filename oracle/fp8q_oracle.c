@@ -190,8 +190,14 @@ uint8_t oracle_fp8_encode(double y, int fmt)
 
 #define ORACLE_BLOCK 128
 
-void oracle_quantize_block(const uint16_t *x, size_t len, int fmt,
-                           uint8_t *q, float *scale)
+/* Element accessors: the block step reads bf16 inputs (widened exactly) or
+ * fp32 inputs (the requantize of a reduced sum). */
+static float elem_bf16(const void *p, size_t i) { return oracle_bf16_to_f32(((const uint16_t *)p)[i]); }
+static float elem_f32(const void *p, size_t i) { return ((const float *)p)[i]; }
+
+/* One block of `len` values: amax, scale, codes. */
+static void quantize_block_any(const void *x, float (*elem)(const void *, size_t), size_t len,
+                               int fmt, uint8_t *q, float *scale)
 {
     const float fmax = (float)oracle_fp8_max(fmt);
     const float smin = ldexpf(1.0f, -126);
@@ -199,7 +205,7 @@ void oracle_quantize_block(const uint16_t *x, size_t len, int fmt,
     size_t i;
 
     for (i = 0; i < len; ++i) {
-        float v = oracle_bf16_to_f32(x[i]);
+        float v = elem(x, i);
         if (!isfinite(v)) {
             *scale = f32_from_bits(0x7FC00000u);
             for (i = 0; i < len; ++i)
@@ -214,9 +220,15 @@ void oracle_quantize_block(const uint16_t *x, size_t len, int fmt,
         s = smin;
     *scale = s;
     for (i = 0; i < len; ++i) {
-        float qf = oracle_bf16_to_f32(x[i]) / s;   /* fp32 quotient, rounded once */
+        float qf = elem(x, i) / s;   /* fp32 quotient, rounded once */
         q[i] = oracle_fp8_encode((double)qf, fmt);
     }
+}
+
+void oracle_quantize_block(const uint16_t *x, size_t len, int fmt,
+                           uint8_t *q, float *scale)
+{
+    quantize_block_any(x, elem_bf16, len, fmt, q, scale);
 }
 
 void oracle_quantize(const uint16_t *x, size_t n, int fmt, uint8_t *q, float *scales)
@@ -227,6 +239,19 @@ void oracle_quantize(const uint16_t *x, size_t n, int fmt, uint8_t *q, float *sc
         size_t len = n - lo < ORACLE_BLOCK ? n - lo : ORACLE_BLOCK;
         oracle_quantize_block(x + lo, len, fmt, q + lo, scales + b);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tensorwise quantize: one fp32 scale for the whole tensor.                 */
+/* The Pi0.5 page ("How to Speed Up VLA Training Step by Step", the FP8      */
+/* section on TorchAO's Float8Linear with the tensorwise recipe) computes    */
+/* amax, scale and cast per tensor.  READING: the same scale rule and floor  */
+/* as the block path, with the block being the whole tensor.                 */
+/* ------------------------------------------------------------------------ */
+
+void oracle_quantize_tensorwise(const uint16_t *x, size_t n, int fmt, uint8_t *q, float *scale)
+{
+    quantize_block_any(x, elem_bf16, n, fmt, q, scale);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -257,21 +282,51 @@ void oracle_dequantize(const uint8_t *q, const float *scales, size_t n, int fmt,
 /* -0 included).  The output is acc (fp32) or RNE_bf16(acc).                 */
 /* ------------------------------------------------------------------------ */
 
+/* acc over the k peers for element i */
+static float reduce_one(const uint8_t *const *q, const float *const *scales, int k, size_t i, int fmt)
+{
+    float acc = oracle_fp8_decode(q[0][i], fmt) * scales[0][i / ORACLE_BLOCK];
+    int p;
+    for (p = 1; p < k; ++p) {
+        float d = oracle_fp8_decode(q[p][i], fmt) * scales[p][i / ORACLE_BLOCK];
+        acc = acc + d;
+    }
+    return acc;
+}
+
 void oracle_dequant_reduce(const uint8_t *const *q, const float *const *scales, int k,
                            size_t n, int fmt, void *y, int out_bf16)
 {
     size_t i;
-    int p;
     for (i = 0; i < n; ++i) {
-        float acc = oracle_fp8_decode(q[0][i], fmt) * scales[0][i / ORACLE_BLOCK];
-        for (p = 1; p < k; ++p) {
-            float d = oracle_fp8_decode(q[p][i], fmt) * scales[p][i / ORACLE_BLOCK];
-            acc = acc + d;
-        }
+        float acc = reduce_one(q, scales, k, i, fmt);
         if (out_bf16)
             ((uint16_t *)y)[i] = oracle_f32_to_bf16(acc);
         else
             ((float *)y)[i] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantize-reduce, then requantize the reduced chunk: the step after the  */
+/* fused reduce in an FP8 all-reduce, whose all-gather half sends FP8 again  */
+/* ("FP8 Transmission Optimization for VLA Training", "Threshold Changes":   */
+/* the FP8 AllGather).  READING: the reduced fp32 values are block-128       */
+/* quantized directly (no bf16 rounding in between), by the same block step  */
+/* as the bf16 path, into the output format.                                 */
+/* ------------------------------------------------------------------------ */
+
+void oracle_reduce_requantize(const uint8_t *const *q, const float *const *scales, int k,
+                              size_t n, int fmt_in, int fmt_out, uint8_t *q_out, float *s_out)
+{
+    float acc[ORACLE_BLOCK];
+    size_t b, j, nb = (n + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+    for (b = 0; b < nb; ++b) {
+        size_t lo = b * ORACLE_BLOCK;
+        size_t len = n - lo < ORACLE_BLOCK ? n - lo : ORACLE_BLOCK;
+        for (j = 0; j < len; ++j)
+            acc[j] = reduce_one(q, scales, k, lo + j, fmt_in);
+        quantize_block_any(acc, elem_f32, len, fmt_out, q_out + lo, s_out + b);
     }
 }
 
@@ -341,6 +396,49 @@ float oracle_e8m0_decode(uint8_t code)
     if (code == 0xFF)
         return NAN;
     return ldexpf(1.0f, (int)code - 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 receiver side: y = dec_e4m3(q) * 2^(code-127) per 32 along K, and   */
+/* the k-peer ordered fp32 sum of such values.  The pages check that the     */
+/* trainer's and the receiver's E8M0 zero-scale clamp agree ("perf: Reduce   */
+/* MXFP8 refit weight-transfer overheads", self-review, "Verified clean").   */
+/* The product is exact in fp32 (a 4-bit significand times a power of two   */
+/* no smaller than 2^-127).  READING: output fp32, or bf16 = RNE of it.      */
+/* ------------------------------------------------------------------------ */
+
+static float mx_value(const uint8_t *q, const uint8_t *e8m0, size_t K, size_t r, size_t c)
+{
+    return oracle_fp8_decode(q[r * K + c], ORACLE_E4M3) *
+           oracle_e8m0_decode(e8m0[r * (K / ORACLE_MX_BLOCK) + c / ORACLE_MX_BLOCK]);
+}
+
+int oracle_mx8_dequant_reduce(const uint8_t *const *q, const uint8_t *const *e8m0, int k,
+                              size_t rows, size_t K, void *y, int out_bf16)
+{
+    size_t r, c;
+    int p;
+    if (K % ORACLE_MX_BLOCK != 0)
+        return -1;
+    for (r = 0; r < rows; ++r)
+        for (c = 0; c < K; ++c) {
+            float acc = mx_value(q[0], e8m0[0], K, r, c);
+            for (p = 1; p < k; ++p) {
+                float d = mx_value(q[p], e8m0[p], K, r, c);
+                acc = acc + d;
+            }
+            if (out_bf16)
+                ((uint16_t *)y)[r * K + c] = oracle_f32_to_bf16(acc);
+            else
+                ((float *)y)[r * K + c] = acc;
+        }
+    return 0;
+}
+
+int oracle_mx8_dequantize(const uint8_t *q, const uint8_t *e8m0, size_t rows, size_t K,
+                          void *y, int out_bf16)
+{
+    return oracle_mx8_dequant_reduce(&q, &e8m0, 1, rows, K, y, out_bf16);
 }
 
 /* Vectorised converter entry points, for exhaustive tests. */

@@ -27,10 +27,21 @@ def digests():
         out["dequantize_tiny_seed0_%s_f32" % name] = oracle.dequantize(qs[0], ss[0], fmt)
         out["reduce_tiny_k4_%s_f32" % name] = oracle.dequant_reduce(list(qs), list(ss), fmt)
         out["reduce_tiny_k4_%s_bf16" % name] = oracle.dequant_reduce(list(qs), list(ss), fmt, True)
+        rq, rs = oracle.reduce_requantize(list(qs), list(ss), fmt, fmt)
+        out["reduce_requantize_tiny_k4_%s_q" % name] = rq
+        out["reduce_requantize_tiny_k4_%s_scales" % name] = rs
+        tq, ts = oracle.quantize_tensorwise(xs[0], fmt)
+        out["quantize_tensorwise_tiny_seed0_%s_q" % name] = tq
+        out["quantize_tensorwise_tiny_seed0_%s_scale" % name] = ts
     w = workloads.bits(workloads.kaiming_uniform((4, 768, 2048), seed=0))
     q, e = oracle.mx8_quantize(w)
     out["mx8_kaiming_4x768x2048_q"] = q
     out["mx8_kaiming_4x768x2048_e8m0"] = e
+    q2 = q.reshape(-1, 2048)
+    out["mx8_dequantize_kaiming_4x768x2048_f32"] = oracle.mx8_dequantize(q2, e)
+    w2 = workloads.bits(workloads.kaiming_uniform((4, 768, 2048), seed=1))
+    qb, eb = oracle.mx8_quantize(w2)
+    out["mx8_reduce_kaiming_k2_f32"] = oracle.mx8_dequant_reduce([q2, qb.reshape(-1, 2048)], [e, eb])
     return {k: hashlib.sha256(v.tobytes()).hexdigest() for k, v in out.items()}
 
 

@@ -8,12 +8,14 @@ must pass the same run.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "fp8q_oracle.c")
-PINS = ["tests/test_oracle_codec.py", "tests/test_oracle_quantize.py", "tests/test_oracle_mx8.py"]
+PINS = ["tests/test_oracle_codec.py", "tests/test_oracle_quantize.py", "tests/test_oracle_mx8.py",
+        "tests/test_oracle_next.py"]
 
 MUTANTS = {
     "e4m3_max_480": ("return fmt == ORACLE_E4M3 ? 448.0 : 57344.0;",
@@ -30,15 +32,29 @@ MUTANTS = {
     "no_scale_floor": ("    if (s < smin)\n        s = smin;\n    *scale = s;",
                        "    *scale = s;"),
     "quotient_not_rounded_to_fp32": (
-        "float qf = oracle_bf16_to_f32(x[i]) / s;   /* fp32 quotient, rounded once */\n"
+        "float qf = elem(x, i) / s;   /* fp32 quotient, rounded once */\n"
         "        q[i] = oracle_fp8_encode((double)qf, fmt);",
-        "double qf = (double)oracle_bf16_to_f32(x[i]) / (double)s;\n"
+        "double qf = (double)elem(x, i) / (double)s;\n"
         "        q[i] = oracle_fp8_encode(qf, fmt);"),
-    "nonfinite_only_nan": ("        if (!isfinite(v)) {\n            *scale",
-                           "        if (isnan(v)) {\n            *scale"),
+    "nonfinite_only_nan": ("        float v = elem(x, i);\n        if (!isfinite(v)) {",
+                           "        float v = elem(x, i);\n        if (isnan(v)) {"),
     "reduce_scale_index": ("float d = oracle_fp8_decode(q[p][i], fmt) * scales[p][i / ORACLE_BLOCK];",
                            "float d = oracle_fp8_decode(q[p][i], fmt) * scales[p][i / 64];"),
-    "reduce_drops_last_peer": ("for (p = 1; p < k; ++p) {", "for (p = 1; p + 1 < k; ++p) {"),
+    "reduce_first_scale_index": ("float acc = oracle_fp8_decode(q[0][i], fmt) * scales[0][i / ORACLE_BLOCK];",
+                                 "float acc = oracle_fp8_decode(q[0][i], fmt) * scales[0][i % ORACLE_BLOCK];"),
+    "requantize_to_input_format": ("quantize_block_any(acc, elem_f32, len, fmt_out, q_out + lo, s_out + b);",
+                                   "quantize_block_any(acc, elem_f32, len, fmt_in, q_out + lo, s_out + b);"),
+    "requantize_through_bf16": ("static float elem_f32(const void *p, size_t i) { return ((const float *)p)[i]; }",
+                                "static float elem_f32(const void *p, size_t i) { return oracle_bf16_to_f32(oracle_f32_to_bf16(((const float *)p)[i])); }"),
+    "tensorwise_first_block_only": ("    quantize_block_any(x, elem_bf16, n, fmt, q, scale);\n}",
+                                    "    quantize_block_any(x, elem_bf16, n < 128 ? n : 128, fmt, q, scale);\n    { size_t i; for (i = 128; i < n; ++i) q[i] = oracle_fp8_encode((double)(elem_bf16(x, i) / *scale), fmt); }\n}"),
+    "mx_dequant_exponent_off": ("    return ldexpf(1.0f, (int)code - 127);", "    return ldexpf(1.0f, (int)code - 126);"),
+    "mx_dequant_row_stride": ("oracle_e8m0_decode(e8m0[r * (K / ORACLE_MX_BLOCK) + c / ORACLE_MX_BLOCK]);",
+                              "oracle_e8m0_decode(e8m0[r + c / ORACLE_MX_BLOCK]);"),
+    "mx_reduce_drops_peer": ("            for (p = 1; p < k; ++p) {\n                float d = mx_value",
+                             "            for (p = 2; p < k; ++p) {\n                float d = mx_value"),
+    "reduce_drops_last_peer": ("    for (p = 1; p < k; ++p) {\n        float d = oracle_fp8_decode",
+                               "    for (p = 1; p + 1 < k; ++p) {\n        float d = oracle_fp8_decode"),
     "reduce_in_double": ("            acc = acc + d;", "            acc = (float)((double)acc + (double)d + 0x1p-60);"),
     "dequant_scale_index": ("float d = oracle_fp8_decode(q[i], fmt) * scales[i / ORACLE_BLOCK];",
                             "float d = oracle_fp8_decode(q[i], fmt) * scales[i / 128 / 2];"),
@@ -68,6 +84,15 @@ def _build(src_text, tmp_path, name):
     return str(so)
 
 
+def _check_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    if text.count(old) != 1:
+        return name + ": anchor not found exactly once"
+    so = _build(text.replace(old, new), tmp_path, name)
+    return None if _run_pins(so, tmp_path) != 0 else name + ": not caught"
+
+
 @pytest.mark.slow
 def test_unmodified_oracle_passes(tmp_path):
     so = _build(open(SRC).read(), tmp_path, "clean")
@@ -75,10 +100,10 @@ def test_unmodified_oracle_passes(tmp_path):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
-    text = open(SRC).read()
-    assert text.count(old) == 1, "mutation anchor not found exactly once: " + name
-    so = _build(text.replace(old, new), tmp_path, name)
-    assert _run_pins(so, tmp_path) != 0, "pins did not catch mutant " + name
+def test_every_mutant_is_caught(tmp_path):
+    # the pin runs are separate processes; run them side by side
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        problems = list(ex.map(lambda m: _check_mutant(m, tmp_path), sorted(MUTANTS)))
+    problems = [p for p in problems if p]
+    assert not problems, problems

@@ -154,10 +154,39 @@ def median_ms(torch, fns):
     return v[len(v) // 2]
 
 
+def graph_ms(torch, fns, replays=5):
+    """Per-launch device time of back-to-back launches: the launches are
+    captured once into a HIP graph (torch.cuda.CUDAGraph) and the graph is
+    replayed, so host-side enqueue time never shows up between kernels."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / (replays * len(fns))
+    del g
+    return ms
+
+
 def payload_sweep(torch, fq, workloads, dev, reps=20):
     """e5m2 block quantize and k = 8 fused reduce (fp32 out) at the payload
     sizes of the sweep, each launch on a different window of 2 GiB pools so
-    that the timed bytes come from HBM, not the 256 MB Infinity Cache."""
+    that the timed bytes come from HBM, not the 256 MB Infinity Cache.
+    Times are per launch of a graph of back-to-back launches."""
     n_pool = 1 << 30
     x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)
     q = torch.empty(n_pool, dtype=torch.uint8, device=dev)
@@ -184,10 +213,8 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
             yo = (i * n) % ((1 << 28) - n) // 4 * 4
             return lambda: fq.fp8q_dequant_reduce(qs, ss, fq.E5M2, out=y[yo:yo + n])
 
-        for fn in [quant(i) for i in range(3)] + [red(i) for i in range(3)]:
-            fn()
-        qm = median_ms(torch, [quant(i) for i in range(reps)])
-        rm = median_ms(torch, [red(i) for i in range(reps)])
+        qm = graph_ms(torch, [quant(i) for i in range(reps)])
+        rm = graph_ms(torch, [red(i) for i in range(reps)])
         out.append({"payload_bytes": nbytes, "elements": n,
                     "quantize_us": round(qm * 1e3, 2),
                     "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
@@ -197,6 +224,68 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
                     "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1)})
     del x, q, s, y
     return out
+
+
+def next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out, reps=10):
+    """The rows beyond the step, on the step's own data:
+    - dequant-reduce -> requantize (e4m3 -> e4m3) of the 8 Pi0.5 shards;
+    - MXFP8 dequantize of the MoE layer (bf16 out, as the receiver's weights)
+      and an 8-peer MXFP8 reduce of gate-shaped expert tensors (fp32 out);
+    - tensorwise e4m3 quantize of the 3.5e9-element gradient."""
+    res = {}
+    n = qs[0].numel()
+    k = len(qs)
+    q_o = torch.empty(n, dtype=torch.uint8, device=dev)
+    s_o = torch.empty(fq.num_scales(n), dtype=torch.float32, device=dev)
+    f = lambda: fq.fp8q_dequant_reduce_requantize(qs, ss, fq.E4M3, fq.E4M3, q_out=q_o, scales_out=s_o)
+    f()
+    ms = median_ms(torch, [f] * reps)
+    alg = reduce_bytes_per_elem(k, 1 + 4 / 128) * n
+    res["reduce_requantize_k8_e4m3"] = {"elements": n, "us": round(ms * 1e3, 2),
+                                        "hbm_GBps": round(alg / ms / 1e6, 1),
+                                        "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del q_o, s_o
+
+    ys = {name: torch.empty(w.shape, dtype=torch.bfloat16, device=dev) for name, w in moe.items()}
+
+    def deq():
+        for name in moe:
+            fq.mx8_dequantize(mx_out[name][0], mx_out[name][1], out_dtype=torch.bfloat16,
+                              out=ys[name])
+    deq()
+    ms = median_ms(torch, [deq] * reps)
+    n_mx = sum(w.numel() for w in moe.values())
+    alg = (1 + 1 / 32 + 2) * n_mx
+    res["mx8_dequantize_layer_bf16"] = {"elements": n_mx, "us": round(ms * 1e3, 2),
+                                        "hbm_GBps": round(alg / ms / 1e6, 1),
+                                        "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del ys
+    shape = moe["gate"].shape
+    peers = [fq.mx8_quantize(workloads.kaiming_uniform(shape, 100 + p, device=dev)) for p in range(8)]
+    y = torch.empty(shape, dtype=torch.float32, device=dev)
+    f = lambda: fq.mx8_dequant_reduce([a for a, _ in peers], [b for _, b in peers], out=y)
+    f()
+    ms = median_ms(torch, [f] * reps)
+    nn = y.numel()
+    alg = (8 * (1 + 1 / 32) + 4) * nn
+    res["mx8_reduce_k8_f32"] = {"elements": nn, "us": round(ms * 1e3, 2),
+                                "hbm_GBps": round(alg / ms / 1e6, 1),
+                                "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del peers, y
+
+    nx = x.numel()
+    q_t = torch.empty(nx, dtype=torch.uint8, device=dev)
+    s_t = torch.empty(1, dtype=torch.float32, device=dev)
+    f = lambda: fq.fp8q_quantize_tensorwise(x, fq.E4M3, q_out=q_t, scale_out=s_t)
+    f()
+    ms = median_ms(torch, [f] * reps)
+    alg = 5.0 * nx
+    res["quantize_tensorwise_e4m3"] = {"elements": nx, "us": round(ms * 1e3, 2),
+                                       "hbm_GBps": round(alg / ms / 1e6, 1),
+                                       "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
+                                       "bytes_per_element": 5}
+    del q_t, s_t
+    return res
 
 
 def stress_reduce(torch, fq, workloads, dev, reps=20):
@@ -220,11 +309,8 @@ def stress_reduce(torch, fq, workloads, dev, reps=20):
 
         full = lambda: fq.fp8q_dequant_reduce([a for a, _ in shards], [b for _, b in shards], fmt,
                                               out_dtype=torch.bfloat16, out=y)
-        for i in range(3):
-            share(i)()
-            full()
-        sm = median_ms(torch, [share(i) for i in range(reps)])
-        fm = median_ms(torch, [full for _ in range(reps)])
+        sm = graph_ms(torch, [share(i) for i in range(reps)])
+        fm = graph_ms(torch, [full for _ in range(reps)])
         alg = reduce_bytes_per_elem(8, 2)
         res[name] = {"share_elements": c, "share_us": round(sm * 1e3, 2),
                      "share_hbm_GBps": round(alg * c / sm / 1e6, 1),
@@ -369,6 +455,8 @@ def main():
         side["naive_dequant_then_sum_k8_us"] = round(naive_ms * 1e3, 2)
         side["fused_speedup_vs_naive"] = round(naive_ms / r_ms, 2)
         del parts
+        log("side figures: requantize, MXFP8 receiver, tensorwise")
+        side.update(next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out))
         log("side figures: payload sweep (e5m2) and stress reduce (bf16 out)")
         side["payload_sweep_e5m2"] = payload_sweep(torch, fq, workloads, dev)
         side["stress_reduce_k8_bf16"] = stress_reduce(torch, fq, workloads, dev)

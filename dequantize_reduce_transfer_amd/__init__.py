@@ -13,6 +13,10 @@ Functions (same names as the C entry points):
   fp8q_dequant_reduce(qs, ss, fmt)     -> y f32 or bf16 [n]
   mx8_quantize(w)                      -> (q uint8 w.shape, e8m0 uint8 [rows, K/32])
   fp8q_sum_f32(parts)                  -> y f32 or bf16 [n]
+  fp8q_dequant_reduce_requantize(qs, ss, fmt_in, fmt_out) -> (q uint8 [n], scales f32)
+  mx8_dequantize(q, e8m0)              -> y f32 or bf16, q.shape
+  mx8_dequant_reduce(qs, es)           -> y f32 or bf16, q.shape
+  fp8q_quantize_tensorwise(x, fmt)     -> (q uint8 [n], scale f32 [1])
 """
 from __future__ import annotations
 
@@ -35,7 +39,9 @@ LIB_PATH = os.path.join(_PKG, "libfp8q.so")
 _lib = None
 
 EXPORTS = ("fp8q_quantize", "fp8q_dequantize", "fp8q_dequant_reduce", "mx8_quantize",
-           "fp8q_sum_f32", "fp8q_status_str", "fp8q_abi_version")
+           "fp8q_sum_f32", "fp8q_dequant_reduce_requantize", "mx8_dequantize",
+           "mx8_dequant_reduce", "fp8q_quantize_tensorwise", "fp8q_status_str",
+           "fp8q_abi_version")
 
 
 class Fp8qError(RuntimeError):
@@ -62,8 +68,13 @@ def lib() -> ctypes.CDLL:
     L.fp8q_dequant_reduce.argtypes = [PP, PP, I, S, I, P, I, P]
     L.mx8_quantize.argtypes = [P, S, S, P, P, P]
     L.fp8q_sum_f32.argtypes = [PP, I, S, P, I, P]
+    L.fp8q_dequant_reduce_requantize.argtypes = [PP, PP, I, S, I, I, P, P, P]
+    L.mx8_dequantize.argtypes = [P, P, S, S, P, I, P]
+    L.mx8_dequant_reduce.argtypes = [PP, PP, I, S, S, P, I, P]
+    L.fp8q_quantize_tensorwise.argtypes = [P, S, I, P, P, P]
     for f in ("fp8q_quantize", "fp8q_dequantize", "fp8q_dequant_reduce", "mx8_quantize",
-              "fp8q_sum_f32"):
+              "fp8q_sum_f32", "fp8q_dequant_reduce_requantize", "mx8_dequantize",
+              "mx8_dequant_reduce", "fp8q_quantize_tensorwise"):
         getattr(L, f).restype = I
     L.fp8q_status_str.argtypes = [I]
     L.fp8q_status_str.restype = ctypes.c_char_p
@@ -227,3 +238,101 @@ def fp8q_sum_f32(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
     _check(lib().fp8q_sum_f32(_ptrs(parts), k, n, out.data_ptr(), _out_code(out_dtype),
                               _stream(parts[0], stream)), "fp8q_sum_f32")
     return out
+
+
+def fp8q_dequant_reduce_requantize(qs: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+                                   fmt_in: int = E4M3, fmt_out: Optional[int] = None,
+                                   q_out: Optional[torch.Tensor] = None,
+                                   scales_out: Optional[torch.Tensor] = None, stream=None):
+    """Fused reduce of k peers, then block-128 requantize of the fp32 sums."""
+    if fmt_out is None:
+        fmt_out = fmt_in
+    k = len(qs)
+    if k < 1 or k != len(scales) or k > MAX_PEERS:
+        raise ValueError("need 1 .. %d code tensors and as many scale tensors" % MAX_PEERS)
+    n = qs[0].numel()
+    for i, (q, s) in enumerate(zip(qs, scales)):
+        _need(q, torch.uint8, "qs[%d]" % i)
+        _need(s, torch.float32, "scales[%d]" % i)
+        if q.numel() != n or s.numel() < num_scales(n):
+            raise ValueError("peer %d has the wrong size" % i)
+    if q_out is None:
+        q_out = torch.empty(n, dtype=torch.uint8, device=qs[0].device)
+    if scales_out is None:
+        scales_out = torch.empty(num_scales(n), dtype=torch.float32, device=qs[0].device)
+    _need(q_out, torch.uint8, "q_out")
+    _need(scales_out, torch.float32, "scales_out")
+    if q_out.numel() != n or scales_out.numel() != num_scales(n):
+        raise ValueError("q_out must hold n codes and scales_out ceil(n/128) scales")
+    _check(lib().fp8q_dequant_reduce_requantize(_ptrs(qs), _ptrs(scales), k, n, _fmt(fmt_in),
+                                                _fmt(fmt_out), q_out.data_ptr(),
+                                                scales_out.data_ptr(), _stream(qs[0], stream)),
+           "fp8q_dequant_reduce_requantize")
+    return q_out, scales_out
+
+
+def mx8_dequant_reduce(qs: Sequence[torch.Tensor], e8m0s: Sequence[torch.Tensor],
+                       out_dtype=torch.float32, out: Optional[torch.Tensor] = None, stream=None):
+    """Sum over k MXFP8 shards of dec_e4m3(q) * 2^(code - 127), in peer order."""
+    k = len(qs)
+    if k < 1 or k != len(e8m0s) or k > MAX_PEERS:
+        raise ValueError("need 1 .. %d code tensors and as many E8M0 tensors" % MAX_PEERS)
+    shape = qs[0].shape
+    if len(shape) < 1 or shape[-1] % MX_BLOCK:
+        raise ValueError("codes must be [..., K] with K a multiple of 32")
+    K = shape[-1]
+    rows = qs[0].numel() // K if K else 0
+    for i, (q, e) in enumerate(zip(qs, e8m0s)):
+        _need(q, torch.uint8, "qs[%d]" % i)
+        _need(e, torch.uint8, "e8m0s[%d]" % i)
+        if q.shape != shape or e.numel() != rows * (K // MX_BLOCK):
+            raise ValueError("peer %d has the wrong size" % i)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=qs[0].device)
+    _need(out, out_dtype, "out")
+    if out.numel() != qs[0].numel():
+        raise ValueError("out must hold rows * K values")
+    _check(lib().mx8_dequant_reduce(_ptrs(qs), _ptrs(e8m0s), k, rows, K, out.data_ptr(),
+                                    _out_code(out_dtype), _stream(qs[0], stream)),
+           "mx8_dequant_reduce")
+    return out
+
+
+def mx8_dequantize(q: torch.Tensor, e8m0: torch.Tensor, out_dtype=torch.float32,
+                   out: Optional[torch.Tensor] = None, stream=None):
+    """dec_e4m3(q) * 2^(code - 127) per 32-element block along K."""
+    _need(q, torch.uint8, "q")
+    _need(e8m0, torch.uint8, "e8m0")
+    if q.dim() < 1 or q.shape[-1] % MX_BLOCK:
+        raise ValueError("codes must be [..., K] with K a multiple of 32")
+    K = q.shape[-1]
+    rows = q.numel() // K if K else 0
+    if e8m0.numel() != rows * (K // MX_BLOCK):
+        raise ValueError("e8m0 must hold rows * K / 32 bytes")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    _need(out, out_dtype, "out")
+    if out.numel() != q.numel():
+        raise ValueError("out must hold rows * K values")
+    _check(lib().mx8_dequantize(q.data_ptr(), e8m0.data_ptr(), rows, K, out.data_ptr(),
+                                _out_code(out_dtype), _stream(q, stream)), "mx8_dequantize")
+    return out
+
+
+def fp8q_quantize_tensorwise(x: torch.Tensor, fmt: int = E4M3, q_out: Optional[torch.Tensor] = None,
+                             scale_out: Optional[torch.Tensor] = None, stream=None):
+    """One fp32 scale for the whole tensor -> (q uint8 [n], scale f32 [1])."""
+    _need(x, torch.bfloat16, "x")
+    n = x.numel()
+    if q_out is None:
+        q_out = torch.empty(n, dtype=torch.uint8, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _need(q_out, torch.uint8, "q_out")
+    _need(scale_out, torch.float32, "scale_out")
+    if q_out.numel() != n or scale_out.numel() != 1:
+        raise ValueError("q_out must hold n codes and scale_out one scale")
+    _check(lib().fp8q_quantize_tensorwise(x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(),
+                                          scale_out.data_ptr(), _stream(x, stream)),
+           "fp8q_quantize_tensorwise")
+    return q_out, scale_out

@@ -122,6 +122,82 @@ fp8q_status fp8q_sum_f32(const float *const *parts, int k, size_t n, void *y_out
                                        static_cast<hipStream_t>(stream)));
 }
 
+fp8q_status fp8q_dequant_reduce_requantize(const void *const *q_peers,
+                                           const float *const *scales_peers, int k, size_t n,
+                                           fp8q_format fmt_in, fp8q_format fmt_out, void *q_out,
+                                           float *scales_out, void *stream) {
+  if (!valid_fmt(fmt_in) || !valid_fmt(fmt_out)) return FP8Q_ERR_ARG;
+  if (k < 1 || k > FP8Q_MAX_PEERS) return FP8Q_ERR_ARG;
+  if (n == 0) return FP8Q_OK;
+  if (n > FP8Q_MAX_ELEMS) return FP8Q_ERR_ARG;
+  if (!q_peers || !scales_peers || !q_out || !scales_out) return FP8Q_ERR_NULL;
+  for (int p = 0; p < k; ++p)
+    if (!q_peers[p] || !scales_peers[p]) return FP8Q_ERR_NULL;
+  if (!aligned(q_out, 16) || !aligned(scales_out, 4)) return FP8Q_ERR_ALIGN;
+  for (int p = 0; p < k; ++p)
+    if (!aligned(q_peers[p], 16) || !aligned(scales_peers[p], 4)) return FP8Q_ERR_ALIGN;
+  const size_t sb = 4 * num_blocks(n, FP8Q_BLOCK);
+  if (overlaps(q_out, n, scales_out, sb)) return FP8Q_ERR_OVERLAP;
+  for (int p = 0; p < k; ++p)
+    if (overlaps(q_out, n, q_peers[p], n) || overlaps(q_out, n, scales_peers[p], sb) ||
+        overlaps(scales_out, sb, q_peers[p], n) || overlaps(scales_out, sb, scales_peers[p], sb))
+      return FP8Q_ERR_OVERLAP;
+  return from_hip(fp8q::launch_reduce_requantize((int)fmt_in, (int)fmt_out, k, q_peers,
+                                                 scales_peers, n, q_out, scales_out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status mx8_dequant_reduce(const void *const *q_peers, const void *const *e8m0_peers, int k,
+                               size_t rows, size_t K, void *y_out, fp8q_out_dtype out_dtype,
+                               void *stream) {
+  if (!valid_out(out_dtype)) return FP8Q_ERR_ARG;
+  if (k < 1 || k > FP8Q_MAX_PEERS) return FP8Q_ERR_ARG;
+  if (K % FP8Q_MX_BLOCK != 0) return FP8Q_ERR_ARG;
+  if (rows == 0 || K == 0) return FP8Q_OK;
+  if (rows > FP8Q_MAX_ELEMS || K > FP8Q_MAX_ELEMS || rows > FP8Q_MAX_ELEMS / K)
+    return FP8Q_ERR_ARG;
+  const size_t n = rows * K;
+  if (!q_peers || !e8m0_peers || !y_out) return FP8Q_ERR_NULL;
+  for (int p = 0; p < k; ++p)
+    if (!q_peers[p] || !e8m0_peers[p]) return FP8Q_ERR_NULL;
+  if (!aligned(y_out, 16)) return FP8Q_ERR_ALIGN;
+  for (int p = 0; p < k; ++p)
+    if (!aligned(q_peers[p], 16)) return FP8Q_ERR_ALIGN;
+  const size_t yb = out_elem_bytes(out_dtype) * n;
+  const size_t eb = n / FP8Q_MX_BLOCK;
+  for (int p = 0; p < k; ++p)
+    if (overlaps(y_out, yb, q_peers[p], n) || overlaps(y_out, yb, e8m0_peers[p], eb))
+      return FP8Q_ERR_OVERLAP;
+  return from_hip(fp8q::launch_mx8_dequant_reduce(k, out_dtype == FP8Q_OUT_BF16, q_peers,
+                                                  e8m0_peers, n, y_out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+fp8q_status mx8_dequantize(const void *q, const void *e8m0, size_t rows, size_t K, void *y_out,
+                           fp8q_out_dtype out_dtype, void *stream) {
+  if (!valid_out(out_dtype)) return FP8Q_ERR_ARG;
+  if (K % FP8Q_MX_BLOCK != 0) return FP8Q_ERR_ARG;
+  if (rows == 0 || K == 0) return FP8Q_OK;
+  if (!q || !e8m0) return FP8Q_ERR_NULL;
+  const void *qp[1] = {q};
+  const void *ep[1] = {e8m0};
+  return mx8_dequant_reduce(qp, ep, 1, rows, K, y_out, out_dtype, stream);
+}
+
+fp8q_status fp8q_quantize_tensorwise(const void *x_bf16, size_t n, fp8q_format fmt, void *q_out,
+                                     float *scale_out, void *stream) {
+  if (!valid_fmt(fmt)) return FP8Q_ERR_ARG;
+  if (n == 0) return FP8Q_OK;
+  if (n > FP8Q_MAX_ELEMS) return FP8Q_ERR_ARG;
+  if (!x_bf16 || !q_out || !scale_out) return FP8Q_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_out, 16) || !aligned(scale_out, 4)) return FP8Q_ERR_ALIGN;
+  if (overlaps(x_bf16, 2 * n, q_out, n) || overlaps(x_bf16, 2 * n, scale_out, 4) ||
+      overlaps(q_out, n, scale_out, 4))
+    return FP8Q_ERR_OVERLAP;
+  return from_hip(fp8q::launch_quantize_tensorwise((int)fmt, x_bf16, n, q_out, scale_out,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 const char *fp8q_status_str(fp8q_status s) {
   switch (s) {
     case FP8Q_OK: return "FP8Q_OK: success";

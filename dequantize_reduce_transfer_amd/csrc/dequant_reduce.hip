@@ -165,6 +165,251 @@ hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t
 }
 
 // ---------------------------------------------------------------------------
+// Dequant-reduce, then requantize the reduced chunk (the all-gather half of
+// an FP8 all-reduce sends FP8 again: "FP8 Transmission Optimization for VLA
+// Training", "Threshold Changes" bullet).  The fp32 sums acc_i are block-128
+// quantized directly: amax over the block, s = max(fl32(amax / FP8_MAX),
+// 2^-126), q_i = satRNE(fl32(acc_i / s)).  The sums are fp32 (24-bit
+// significands), outside the bf16 domain the quantize kernel's divide-free
+// quotient was proven on, so each element uses the IEEE divide; the VALU
+// budget of this kernel (k reads per element) has room for it.
+//
+// Same mapping as reduce_kernel: lanes 0-31 of a 256-element group hold one
+// block, lanes 32-63 the next; the block amax is 4 DPP steps within each
+// 16-lane row plus one swap of rows 0<->1 and 2<->3.
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+struct F32Scale {
+  float s;
+  bool finite;
+};
+
+template <int FMT>
+__device__ __forceinline__ F32Scale f32_block_scale(uint32_t amax_bits) {
+  F32Scale r;
+  r.finite = amax_bits < 0x7F800000u;
+  float s = __uint_as_float(amax_bits) / fp8_max<FMT>();    // IEEE fp32 divide
+  s = fmaxf(s, 0x1p-126f);
+  r.s = r.finite ? s : __uint_as_float(0x7FC00000u);
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ float f32_quot(float v, float s) {
+  return __builtin_amdgcn_fmed3f(v / s, -fp8_max<FMT>(), fp8_max<FMT>());   // IEEE divide
+}
+
+// Elements [start, n) (start is block-aligned): one block per pass, two
+// elements per lane, a whole-wave amax.
+template <int FIN, int FOUT, int K>
+__device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float *__restrict__ so,
+                             uint64_t n, uint64_t start) {
+  const uint32_t lane = lane_id();
+  for (uint64_t b0 = start; b0 < n; b0 += kBlock) {
+    float v[2];
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint64_t i = b0 + 2 * lane + j;
+      v[j] = 0.0f;
+      if (i < n) {
+        const uint64_t blk = i / kBlock;
+        float acc = dec1<FIN>(reinterpret_cast<const uint8_t *>(P.q[0])[i]) * P.s[0][blk];
+#pragma unroll
+        for (int p = 1; p < K; ++p) {
+          const float d = dec1<FIN>(reinterpret_cast<const uint8_t *>(P.q[p])[i]) * P.s[p][blk];
+          acc = acc + d;
+        }
+        v[j] = acc;
+        m = m > abs_bits(acc) ? m : abs_bits(acc);
+      }
+    }
+    const F32Scale sc = f32_block_scale<FOUT>(max_wave(m));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint64_t i = b0 + 2 * lane + j;
+      if (i < n) {
+        const uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(v[j], sc.s), 0.0f, 0.0f, 0.0f);
+        qo[i] = sc.finite ? (uint8_t)c : (uint8_t)0x7F;
+      }
+    }
+    if (lane == 0) so[b0 / kBlock] = sc.s;
+  }
+}
+
+template <int FIN, int FOUT, int K, int U>
+__global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
+                                                      float *__restrict__ so, uint64_t n,
+                                                      uint64_t full_tiles) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  constexpr uint64_t kTileBlocks = kTile / kBlock;
+  const uint32_t lane = lane_id();
+  const bool upper = lane >= 32;
+  const uint64_t nw = wave_count();
+  const uint64_t w0 = wave_index();
+
+  for (uint64_t t = w0; t < full_tiles; t += nw) {
+    const uint64_t dw0 = t * (kTile / 4);
+    uint32_t w[K][U];
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+
+    float acc[U][4];
+#pragma unroll
+    for (int p = 0; p < K; ++p) {
+      const float *sp = P.s[p] + t * kTileBlocks;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float s = upper ? sp[2 * u + 1] : sp[2 * u];
+        const f32x2 lo = dec2<FIN, false>(w[p][u]);
+        const f32x2 hi = dec2<FIN, true>(w[p][u]);
+        const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
+        if (p == 0) {
+          acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
+        } else {
+          acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
+          acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t m = abs_bits(acc[u][0]);
+#pragma unroll
+      for (int j = 1; j < 4; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
+      const F32Scale sc = f32_block_scale<FOUT>(max_half32(m));
+      uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(acc[u][0], sc.s), f32_quot<FOUT>(acc[u][1], sc.s),
+                              f32_quot<FOUT>(acc[u][2], sc.s), f32_quot<FOUT>(acc[u][3], sc.s));
+      if (!sc.finite) c = 0x7F7F7F7Fu;
+      st(qo + dw0 + u * kWave + lane, c);
+      if ((lane & 31) == 0) so[t * kTileBlocks + 2 * u + (upper ? 1 : 0)] = sc.s;
+    }
+  }
+  if (w0 == nw - 1)
+    requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
+}
+
+template <int FIN, int FOUT, int K>
+hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
+  constexpr int U = reduce_u<K>();
+  const uint64_t full = n / ((uint64_t)U * 256);
+  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U>), dim3(grid_for_tiles(full)), dim3(256), 0,
+                     stream, P, static_cast<uint32_t *>(qo), so, n, full);
+  return hipGetLastError();
+}
+
+template <int FIN, int FOUT, int K = 1>
+hipError_t dispatch_requant_k(int k, const PeerPtrs &P, uint64_t n, void *qo, float *so,
+                              hipStream_t stream) {
+  if constexpr (K > kMaxPeers) {
+    return hipErrorInvalidValue;
+  } else {
+    if (k == K) return launch_requant_t<FIN, FOUT, K>(P, n, qo, so, stream);
+    return dispatch_requant_k<FIN, FOUT, K + 1>(k, P, n, qo, so, stream);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 receiver side: y = sum over peers of dec_e4m3(q_p) * 2^(code_p - 127)
+// per 32-element block ("perf: Reduce MXFP8 refit weight-transfer
+// overheads": the receiver of the prequantized weights; its E8M0 zero-scale
+// clamp must agree with the trainer's).  The [rows, K] codes and the
+// [rows, K/32] scale bytes are both flat in block order (K % 32 == 0), so the
+// kernel runs over n = rows * K elements.  Each 4-code dword of a lane lies in
+// one 32-element block; its E8M0 byte is loaded per lane (8 lanes share it).
+// 2^(code-127) is built from bits: code 0 is the fp32 subnormal 2^-127 and
+// 0xFF is NaN.  Each product is exact; the sum is in peer order.
+
+struct MxPeerPtrs {
+  const uint32_t *q[kMaxPeers];
+  const uint8_t *e[kMaxPeers];
+};
+
+__device__ __forceinline__ float e8m0_value(uint32_t code) {
+  const uint32_t bits = code == 0u ? 0x00400000u : (code == 0xFFu ? 0x7FC00000u : code << 23);
+  return __uint_as_float(bits);
+}
+
+template <int K, bool BF16>
+__device__ void mx_reduce_tail(const MxPeerPtrs &P, void *__restrict__ y, uint64_t n, uint64_t start) {
+  for (uint64_t i = start + lane_id(); i < n; i += kWave) {
+    const uint64_t blk = i / kMxBlock;
+    float acc = dec1<0>(reinterpret_cast<const uint8_t *>(P.q[0])[i]) * e8m0_value(P.e[0][blk]);
+#pragma unroll
+    for (int p = 1; p < K; ++p) {
+      const float d = dec1<0>(reinterpret_cast<const uint8_t *>(P.q[p])[i]) * e8m0_value(P.e[p][blk]);
+      acc = acc + d;
+    }
+    store1<BF16>(y, i, acc);
+  }
+}
+
+template <int K, int U, bool BF16>
+__global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__restrict__ y,
+                                                        uint64_t n, uint64_t full_tiles) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  const uint32_t lane = lane_id();
+  const uint64_t nw = wave_count();
+  const uint64_t w0 = wave_index();
+
+  for (uint64_t t = w0; t < full_tiles; t += nw) {
+    const uint64_t dw0 = t * (kTile / 4);
+    uint32_t w[K][U];
+    uint32_t c[K][U];
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+        c[p][u] = P.e[p][(t * kTile + (uint64_t)u * 256) / kMxBlock + lane / 8];
+      }
+    float acc[U][4];
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float s = e8m0_value(c[p][u]);
+        const f32x2 lo = dec2<0, false>(w[p][u]);
+        const f32x2 hi = dec2<0, true>(w[p][u]);
+        const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
+        if (p == 0) {
+          acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
+        } else {
+          acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
+          acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
+                   acc[u][3]);
+  }
+  if (w0 == nw - 1) mx_reduce_tail<K, BF16>(P, y, n, full_tiles * kTile);
+}
+
+template <int K, bool BF16>
+hipError_t launch_mx_reduce_t(const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
+  constexpr int U = reduce_u<K>();
+  const uint64_t full = n / ((uint64_t)U * 256);
+  hipLaunchKernelGGL((mx_reduce_kernel<K, U, BF16>), dim3(grid_for_tiles(full)), dim3(256), 0,
+                     stream, P, y, n, full);
+  return hipGetLastError();
+}
+
+template <bool BF16, int K = 1>
+hipError_t dispatch_mx_k(int k, const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
+  if constexpr (K > kMaxPeers) {
+    return hipErrorInvalidValue;
+  } else {
+    if (k == K) return launch_mx_reduce_t<K, BF16>(P, n, y, stream);
+    return dispatch_mx_k<BF16, K + 1>(k, P, n, y, stream);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Naive comparator: y = ((p_0 + p_1) + ...) over k fp32 arrays.
 
 template <bool BF16>
@@ -203,6 +448,32 @@ hipError_t launch_dequant_reduce(int fmt, int k, bool out_bf16, const void *cons
                     : dispatch_k<0, false>(k, P, n, y, stream);
   return out_bf16 ? dispatch_k<1, true>(k, P, n, y, stream)
                   : dispatch_k<1, false>(k, P, n, y, stream);
+}
+
+hipError_t launch_reduce_requantize(int fmt_in, int fmt_out, int k, const void *const *q,
+                                   const float *const *scales, uint64_t n, void *q_out,
+                                   float *scales_out, hipStream_t stream) {
+  PeerPtrs P = {};
+  for (int p = 0; p < k; ++p) {
+    P.q[p] = static_cast<const uint32_t *>(q[p]);
+    P.s[p] = scales[p];
+  }
+  if (fmt_in == 0)
+    return fmt_out == 0 ? dispatch_requant_k<0, 0>(k, P, n, q_out, scales_out, stream)
+                        : dispatch_requant_k<0, 1>(k, P, n, q_out, scales_out, stream);
+  return fmt_out == 0 ? dispatch_requant_k<1, 0>(k, P, n, q_out, scales_out, stream)
+                      : dispatch_requant_k<1, 1>(k, P, n, q_out, scales_out, stream);
+}
+
+hipError_t launch_mx8_dequant_reduce(int k, bool out_bf16, const void *const *q,
+                                     const void *const *e8m0, uint64_t n, void *y,
+                                     hipStream_t stream) {
+  MxPeerPtrs P = {};
+  for (int p = 0; p < k; ++p) {
+    P.q[p] = static_cast<const uint32_t *>(q[p]);
+    P.e[p] = static_cast<const uint8_t *>(e8m0[p]);
+  }
+  return out_bf16 ? dispatch_mx_k<true>(k, P, n, y, stream) : dispatch_mx_k<false>(k, P, n, y, stream);
 }
 
 hipError_t launch_sum_f32(int k, bool out_bf16, const float *const *parts, uint64_t n, void *y,

@@ -70,6 +70,21 @@ __device__ __forceinline__ uint32_t max_row16(uint32_t v) {
   return dpp_max<kDppRowMirror>(v);
 }
 
+// Max over a 32-lane half-wave (every lane gets its half's result): rows
+// 0<->1 and 2<->3 are exchanged through the lane crossbar (ds_bpermute).
+__device__ __forceinline__ uint32_t max_half32(uint32_t v) {
+  v = max_row16(v);
+  const uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
+  return v > o ? v : o;
+}
+
+// Max over the whole wave.
+__device__ __forceinline__ uint32_t max_wave(uint32_t v) {
+  v = max_half32(v);
+  const uint32_t o = (uint32_t)__shfl_xor((int)v, 32);
+  return v > o ? v : o;
+}
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Largest sign-cleared bf16 bit pattern among the 8 bf16 held in a u32x4.

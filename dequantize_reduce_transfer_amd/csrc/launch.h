@@ -34,10 +34,25 @@ inline uint32_t grid_for_tiles(uint64_t tiles) {
 hipError_t launch_quantize(int fmt, const void *x, uint64_t n, void *q, float *scales,
                            hipStream_t stream);
 
+// Tensorwise quantize: one fp32 scale for the whole tensor, written to
+// *scale (which also serves as the amax slot while the kernels run).
+hipError_t launch_quantize_tensorwise(int fmt, const void *x, uint64_t n, void *q, float *scale,
+                                      hipStream_t stream);
+
 // Fused dequantize-then-reduce of k shards (k == 1 is a dequantize).
 hipError_t launch_dequant_reduce(int fmt, int k, bool out_bf16, const void *const *q,
                                  const float *const *scales, uint64_t n, void *y,
                                  hipStream_t stream);
+
+// Dequant-reduce of k shards, then block-128 requantize of the fp32 sums.
+hipError_t launch_reduce_requantize(int fmt_in, int fmt_out, int k, const void *const *q,
+                                   const float *const *scales, uint64_t n, void *q_out,
+                                   float *scales_out, hipStream_t stream);
+
+// MXFP8 dequant-reduce of k shards of n = rows * K elements (k == 1: dequantize).
+hipError_t launch_mx8_dequant_reduce(int k, bool out_bf16, const void *const *q,
+                                     const void *const *e8m0, uint64_t n, void *y,
+                                     hipStream_t stream);
 
 // Ordered sum of k fp32 arrays (the naive path's reduction).
 hipError_t launch_sum_f32(int k, bool out_bf16, const float *const *parts, uint64_t n, void *y,

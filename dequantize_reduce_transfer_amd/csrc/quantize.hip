@@ -166,7 +166,107 @@ hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Tensorwise quantize: one fp32 scale for the whole tensor (the tensorwise
+// recipe of TorchAO's Float8Linear on "How to Speed Up VLA Training Step by
+// Step: A 3x Acceleration Case Study on Pi0.5", FP8 section: amax, scale
+// and cast per tensor), with the block rule above applied to one block that
+// spans the tensor.  The global amax needs its own pass, so the bf16 input
+// is read twice (5 B per element).  Four launches on the caller's stream:
+//   1. tw_zero:     the caller's scale slot <- 0 (it holds amax bits first);
+//   2. tw_amax:     grid-stride read-only pass, one atomic max per workgroup;
+//   3. tw_quantize: the quantize mapping above with the scale from the slot;
+//   4. tw_finalize: the slot <- the fp32 scale.
+// Step 3 only reads the slot and step 4 writes it after every wave of step 3
+// has finished (stream order), so no wave ever sees a half-written value.
+
+__global__ __launch_bounds__(64) void tw_zero_kernel(uint32_t *slot) {
+  if (threadIdx.x == 0) *slot = 0u;
+}
+
+__global__ __launch_bounds__(256) void tw_amax_kernel(const u32x4 *__restrict__ x, uint64_t n,
+                                                      uint32_t *__restrict__ slot) {
+  __shared__ uint32_t part[4];
+  const uint64_t nch = n / 8;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint32_t m = 0;
+  for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nch; c += stride) {
+    const uint32_t a = amax_bits8(ld(x + c));
+    m = m > a ? m : a;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
+    const uint32_t a = reinterpret_cast<const uint16_t *>(x)[8 * nch + threadIdx.x] & 0x7FFFu;
+    m = m > a ? m : a;
+  }
+  m = max_wave(m);
+  if (lane_id() == 0) part[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+    for (int i = 1; i < (int)(blockDim.x / kWave); ++i) r = r > part[i] ? r : part[i];
+    atomicMax(slot, r);
+  }
+}
+
+template <int FMT, int U>
+__global__ __launch_bounds__(256) void tw_quantize_kernel(const u32x4 *__restrict__ x,
+                                                          u32x2 *__restrict__ q,
+                                                          const uint32_t *__restrict__ slot,
+                                                          uint64_t n, uint64_t full_tiles) {
+  constexpr uint64_t kChunks = U * kWave;
+  const uint32_t lane = lane_id();
+  const uint64_t nw = wave_count();
+  const uint64_t w0 = wave_index();
+  const BlockScale b = block_scale<FMT>(*slot);
+
+  for (uint64_t t = w0; t < full_tiles; t += nw) {
+    const uint64_t c0 = t * kChunks;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld(x + c0 + u * kWave + lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st(q + c0 + u * kWave + lane, quant8<FMT>(v[u], b));
+  }
+  if (w0 == nw - 1) {
+    const uint16_t *x16 = reinterpret_cast<const uint16_t *>(x);
+    uint8_t *q8 = reinterpret_cast<uint8_t *>(q);
+    for (uint64_t i = full_tiles * kChunks * 8 + lane; i < n; i += kWave) {
+      const uint32_t c = cvt4<FMT>(quotient<FMT>(bf16_lo(x16[i]), b), 0.0f, 0.0f, 0.0f);
+      q8[i] = b.finite ? (uint8_t)c : (uint8_t)0x7F;
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64) void tw_finalize_kernel(uint32_t *slot) {
+  if (threadIdx.x == 0) *slot = __float_as_uint(block_scale<FMT>(*slot).s);
+}
+
+template <int FMT>
+hipError_t launch_tw_t(const void *x, uint64_t n, void *q, float *scale, hipStream_t stream) {
+  constexpr int U = kQuantU;
+  uint32_t *slot = reinterpret_cast<uint32_t *>(scale);
+  hipLaunchKernelGGL(tw_zero_kernel, dim3(1), dim3(64), 0, stream, slot);
+  // the amax pass only reads: a bounded grid-stride grid, so the atomics
+  // number a few thousand at most
+  uint64_t wgs = (n / 8 + 255) / 256;
+  if (wgs > 4096) wgs = 4096;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL(tw_amax_kernel, dim3((uint32_t)wgs), dim3(256), 0, stream,
+                     static_cast<const u32x4 *>(x), n, slot);
+  const uint64_t full = n / ((uint64_t)U * kWave * 8);
+  hipLaunchKernelGGL((tw_quantize_kernel<FMT, U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,
+                     static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), slot, n, full);
+  hipLaunchKernelGGL(tw_finalize_kernel<FMT>, dim3(1), dim3(64), 0, stream, slot);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quantize_tensorwise(int fmt, const void *x, uint64_t n, void *q, float *scale,
+                                      hipStream_t stream) {
+  return fmt == 0 ? launch_tw_t<0>(x, n, q, scale, stream) : launch_tw_t<1>(x, n, q, scale, stream);
+}
 
 hipError_t launch_quantize(int fmt, const void *x, uint64_t n, void *q, float *scales,
                            hipStream_t stream) {

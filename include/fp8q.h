@@ -154,6 +154,61 @@ FP8Q_API fp8q_status mx8_quantize(const void *w_bf16, size_t rows, size_t K, voi
 FP8Q_API fp8q_status fp8q_sum_f32(const float *const *parts, int k, size_t n, void *y_out,
                          fp8q_out_dtype out_dtype, void *stream);
 
+/*
+ * Fused dequant-reduce, then requantize: the reduced chunk leaves as FP8 again
+ * for the all-gather half of an FP8 all-reduce ("FP8 Transmission
+ * Optimization for VLA Training", "Threshold Changes" bullet: the FP8
+ * AllGather).  The fp32 sums acc_i of fp8q_dequant_reduce (format fmt_in)
+ * are block-128 quantized directly into fmt_out, by the rule of
+ * fp8q_quantize applied to fp32 values:
+ *   s_b = max(fl32(amax_b / FP8_MAX_out), 2^-126),  q_i = satRNE(fl32(acc_i / s_b))
+ * A block whose sums hold an inf or NaN gets s_b = NaN and all codes 0x7F.
+ *   q_peers, scales_peers, k   as fp8q_dequant_reduce
+ *   q_out      [n] uint8, device, 16-byte aligned
+ *   scales_out [ceil(n / 128)] fp32, device, 4-byte aligned
+ * The outputs may overlap neither each other nor any peer's input.
+ */
+FP8Q_API fp8q_status fp8q_dequant_reduce_requantize(const void *const *q_peers,
+                                                    const float *const *scales_peers, int k,
+                                                    size_t n, fp8q_format fmt_in,
+                                                    fp8q_format fmt_out, void *q_out,
+                                                    float *scales_out, void *stream);
+
+/*
+ * MXFP8 receiver side ("perf: Reduce MXFP8 refit weight-transfer overheads":
+ * the receiver of the prequantized weights, whose E8M0 zero-scale clamp must
+ * agree with the trainer's -- review "Verified clean").  Per element of the
+ * [rows, K] codes, with the [rows, K/32] E8M0 bytes of mx8_quantize:
+ *   d = dec_e4m3(q) * 2^(code - 127)      (exact in fp32; code 0xFF -> NaN)
+ * mx8_dequant_reduce sums k such shards in peer order, each addition rounded
+ * to fp32; mx8_dequantize is k = 1.  Output fp32, or bf16 (RNE of the fp32).
+ *   q / q_peers        [rows, K] uint8 E4M3 codes, device, 16-byte aligned
+ *   e8m0 / e8m0_peers  [rows, K/32] uint8, device, any alignment
+ *   K                  a multiple of 32;   k   1 .. FP8Q_MAX_PEERS
+ *   y_out              [rows, K] fp32 or bf16, device, 16-byte aligned
+ */
+FP8Q_API fp8q_status mx8_dequantize(const void *q, const void *e8m0, size_t rows, size_t K,
+                                    void *y_out, fp8q_out_dtype out_dtype, void *stream);
+FP8Q_API fp8q_status mx8_dequant_reduce(const void *const *q_peers, const void *const *e8m0_peers,
+                                        int k, size_t rows, size_t K, void *y_out,
+                                        fp8q_out_dtype out_dtype, void *stream);
+
+/*
+ * Tensorwise quantize: one fp32 scale for the whole tensor, the tensorwise
+ * recipe (amax, scale and cast per tensor) named on "How to Speed Up VLA
+ * Training Step by Step: A 3x Acceleration Case Study on Pi0.5", FP8 section.
+ * The rule of fp8q_quantize with one block spanning the tensor:
+ *   s = max(fl32(amax / FP8_MAX), 2^-126),  q_i = satRNE(fl32(x_i / s))
+ * (inf or NaN anywhere: s = NaN, all codes 0x7F).  The input is read twice
+ * (an amax pass, then the quantize pass).  *scale_out is also the amax slot
+ * while the call's kernels run: it holds the scale once they have finished.
+ *   x_bf16     [n] bf16, device, 16-byte aligned
+ *   q_out      [n] uint8, device, 16-byte aligned
+ *   scale_out  one fp32, device, 4-byte aligned
+ */
+FP8Q_API fp8q_status fp8q_quantize_tensorwise(const void *x_bf16, size_t n, fp8q_format fmt,
+                                              void *q_out, float *scale_out, void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 FP8Q_API const char *fp8q_status_str(fp8q_status s);
 

@@ -184,3 +184,66 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fq, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         fq.lib()
+
+
+@no_gpu
+def test_requantize_validation():
+    L = fq.lib()
+    n = 4096
+    qs = [Buf(n) for _ in range(4)]
+    ss = [Buf(4 * 32) for _ in range(4)]
+    qo, so = Buf(n), Buf(4 * 32)
+    qa = PP(*[b.addr for b in qs])
+    sa = PP(*[b.addr for b in ss])
+    f = L.fp8q_dequant_reduce_requantize
+    assert f(qa, sa, 4, n, 0, 2, P(qo.addr), P(so.addr), None) == ERR_ARG
+    assert f(qa, sa, 0, n, 0, 0, P(qo.addr), P(so.addr), None) == ERR_ARG
+    assert f(qa, sa, 17, n, 0, 0, P(qo.addr), P(so.addr), None) == ERR_ARG
+    assert f(None, None, 4, 0, 0, 1, None, None, None) == OK
+    assert f(qa, sa, 4, n, 0, 1, None, P(so.addr), None) == ERR_NULL
+    assert f(qa, sa, 4, n, 0, 1, P(qo.addr), None, None) == ERR_NULL
+    assert f(qa, sa, 4, n, 0, 1, P(qo.addr + 4), P(so.addr), None) == ERR_ALIGN
+    assert f(qa, sa, 4, n, 0, 1, P(qo.addr), P(so.addr + 1), None) == ERR_ALIGN
+    assert f(qa, sa, 4, n, 0, 1, P(qo.addr), P(qo.addr + n - 16), None) == ERR_OVERLAP
+    # in-place over a peer's codes or scales is rejected
+    assert f(qa, sa, 4, n, 0, 1, P(qs[2].addr), P(so.addr), None) == ERR_OVERLAP
+    assert f(qa, sa, 4, n, 0, 1, P(qo.addr), P(ss[3].addr), None) == ERR_OVERLAP
+
+
+@no_gpu
+def test_mx8_receiver_validation():
+    L = fq.lib()
+    rows, K = 16, 256
+    n = rows * K
+    q, e, y = Buf(n), Buf(n // 32), Buf(4 * n)
+    assert L.mx8_dequantize(P(q.addr), P(e.addr), rows, 48, P(y.addr), 0, None) == ERR_ARG
+    assert L.mx8_dequantize(P(q.addr), P(e.addr), rows, K, P(y.addr), 3, None) == ERR_ARG
+    assert L.mx8_dequantize(None, None, 0, K, None, 0, None) == OK
+    assert L.mx8_dequantize(None, P(e.addr), rows, K, P(y.addr), 0, None) == ERR_NULL
+    assert L.mx8_dequantize(P(q.addr), None, rows, K, P(y.addr), 0, None) == ERR_NULL
+    assert L.mx8_dequantize(P(q.addr), P(e.addr), rows, K, None, 0, None) == ERR_NULL
+    assert L.mx8_dequantize(P(q.addr + 8), P(e.addr), rows, K, P(y.addr), 0, None) == ERR_ALIGN
+    assert L.mx8_dequantize(P(q.addr), P(e.addr + 3), rows, K, P(y.addr + 4), 0, None) == ERR_ALIGN
+    assert L.mx8_dequantize(P(q.addr), P(y.addr + 4 * n - 8), rows, K, P(y.addr), 0, None) == ERR_OVERLAP
+    qa = PP(q.addr, q.addr)
+    ea = PP(e.addr, e.addr + 1)       # E8M0 arrays need no alignment
+    assert L.mx8_dequant_reduce(qa, ea, 0, rows, K, P(y.addr), 0, None) == ERR_ARG
+    assert L.mx8_dequant_reduce(qa, ea, 17, rows, K, P(y.addr), 0, None) == ERR_ARG
+    assert L.mx8_dequant_reduce(qa, PP(e.addr, 0), 2, rows, K, P(y.addr), 0, None) == ERR_NULL
+    assert L.mx8_dequant_reduce(PP(q.addr, y.addr), ea, 2, rows, K, P(y.addr), 1, None) == ERR_OVERLAP
+
+
+@no_gpu
+def test_tensorwise_validation():
+    L = fq.lib()
+    n = 1000
+    x, q, s = Buf(2 * n), Buf(n), Buf(16)
+    f = L.fp8q_quantize_tensorwise
+    assert f(P(x.addr), n, 9, P(q.addr), P(s.addr), None) == ERR_ARG
+    assert f(None, 0, 0, None, None, None) == OK
+    assert f(P(x.addr), (1 << 40) + 1, 0, P(q.addr), P(s.addr), None) == ERR_ARG
+    assert f(P(x.addr), n, 0, P(q.addr), None, None) == ERR_NULL
+    assert f(P(x.addr + 2), n, 0, P(q.addr), P(s.addr), None) == ERR_ALIGN
+    assert f(P(x.addr), n, 0, P(q.addr), P(s.addr + 2), None) == ERR_ALIGN
+    assert f(P(x.addr), n, 0, P(q.addr), P(x.addr + 1000), None) == ERR_OVERLAP
+    assert f(P(x.addr), n, 0, P(q.addr), P(q.addr + 996), None) == ERR_OVERLAP

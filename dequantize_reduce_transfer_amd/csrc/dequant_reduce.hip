@@ -28,13 +28,16 @@ namespace fp8q {
 namespace {
 
 #ifndef FP8Q_RED_U4
-#define FP8Q_RED_U4 4        // tile depth for k <= 4
+#define FP8Q_RED_U4 2        // tile depth for k <= 4
 #endif
 #ifndef FP8Q_RED_U8
 #define FP8Q_RED_U8 2        // tile depth for 4 < k <= 8
 #endif
 #ifndef FP8Q_RED_U16
 #define FP8Q_RED_U16 1       // tile depth for 8 < k <= 16
+#endif
+#ifndef FP8Q_RED_T
+#define FP8Q_RED_T 2         // consecutive tiles per wave (pipelined)
 #endif
 
 struct PeerPtrs {
@@ -100,46 +103,74 @@ __device__ void reduce_tail(const PeerPtrs &P, void *__restrict__ y, uint64_t n,
   }
 }
 
+template <int K, int U>
+__device__ __forceinline__ void load_codes(const PeerPtrs &P, uint64_t t, uint32_t lane,
+                                           uint32_t (&w)[K][U]) {
+  const uint64_t dw0 = t * ((uint64_t)U * 64);     // first code dword of tile t
+#pragma unroll
+  for (int p = 0; p < K; ++p)
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+}
+
 template <int FMT, int K, int U, bool BF16>
-__global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restrict__ y, uint64_t n,
-                                                     uint64_t full_tiles) {
+__device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const uint32_t (&w)[K][U],
+                                            void *__restrict__ y, uint64_t t, uint32_t lane) {
   constexpr uint64_t kTile = (uint64_t)U * 256;    // elements per tile
   constexpr uint64_t kTileBlocks = kTile / kBlock; // = 2U
-  const uint32_t lane = lane_id();
   const bool upper = lane >= 32;
+  float acc[U][4];
+#pragma unroll
+  for (int p = 0; p < K; ++p) {
+    const float *sp = P.s[p] + t * kTileBlocks;    // wave-uniform
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = upper ? sp[2 * u + 1] : sp[2 * u];
+      const f32x2 lo = dec2<FMT, false>(w[p][u]);
+      const f32x2 hi = dec2<FMT, true>(w[p][u]);
+      const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
+      if (p == 0) {
+        acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
+      } else {
+        acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
+        acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
+                 acc[u][3]);
+}
+
+// Each wave takes T consecutive tiles; the next tile's code loads are
+// issued before the current tile's arithmetic.
+template <int FMT, int K, int U, int T, bool BF16>
+__global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restrict__ y, uint64_t n,
+                                                     uint64_t full_tiles) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  const uint32_t lane = lane_id();
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t = w0; t < full_tiles; t += nw) {
-    const uint64_t dw0 = t * (kTile / 4);          // first code dword of the tile
-    uint32_t w[K][U];
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    uint32_t cur[K][U];
+    load_codes<K, U>(P, t0, lane, cur);
 #pragma unroll
-    for (int p = 0; p < K; ++p)
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      uint32_t nxt[K][U];
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) load_codes<K, U>(P, t + 1, lane, nxt);
+      reduce_tile<FMT, K, U, BF16>(P, cur, y, t, lane);
+      if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
-
-    float acc[U][4];
+        for (int p = 0; p < K; ++p)
 #pragma unroll
-    for (int p = 0; p < K; ++p) {
-      const float *sp = P.s[p] + t * kTileBlocks;  // wave-uniform
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float s = upper ? sp[2 * u + 1] : sp[2 * u];
-        const f32x2 lo = dec2<FMT, false>(w[p][u]);
-        const f32x2 hi = dec2<FMT, true>(w[p][u]);
-        const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
-        if (p == 0) {
-          acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
-        } else {
-          acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
-          acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
-        }
+          for (int u = 0; u < U; ++u) cur[p][u] = nxt[p][u];
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
-                   acc[u][3]);
   }
   if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
 }
@@ -147,10 +178,11 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = reduce_u<K>();
+  constexpr int T = FP8Q_RED_T;
   const uint64_t tile = (uint64_t)U * 256;
   const uint64_t full = n / tile;
-  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, BF16>), dim3(grid_for_tiles(full)), dim3(256), 0,
-                     stream, P, y, n, full);
+  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
+                     dim3(256), 0, stream, P, y, n, full);
   return hipGetLastError();
 }
 
@@ -239,53 +271,72 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
 }
 
 template <int FIN, int FOUT, int K, int U>
+__device__ __forceinline__ void requant_tile(const PeerPtrs &P, const uint32_t (&w)[K][U],
+                                             uint32_t *__restrict__ qo, float *__restrict__ so,
+                                             uint64_t t, uint32_t lane) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  constexpr uint64_t kTileBlocks = kTile / kBlock;
+  const bool upper = lane >= 32;
+  const uint64_t dw0 = t * (kTile / 4);
+  float acc[U][4];
+#pragma unroll
+  for (int p = 0; p < K; ++p) {
+    const float *sp = P.s[p] + t * kTileBlocks;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = upper ? sp[2 * u + 1] : sp[2 * u];
+      const f32x2 lo = dec2<FIN, false>(w[p][u]);
+      const f32x2 hi = dec2<FIN, true>(w[p][u]);
+      const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
+      if (p == 0) {
+        acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
+      } else {
+        acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
+        acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t m = abs_bits(acc[u][0]);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
+    const F32Scale sc = f32_block_scale<FOUT>(max_half32(m));
+    uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(acc[u][0], sc.s), f32_quot<FOUT>(acc[u][1], sc.s),
+                            f32_quot<FOUT>(acc[u][2], sc.s), f32_quot<FOUT>(acc[u][3], sc.s));
+    if (!sc.finite) c = 0x7F7F7F7Fu;
+    st(qo + dw0 + u * kWave + lane, c);
+    if ((lane & 31) == 0) so[t * kTileBlocks + 2 * u + (upper ? 1 : 0)] = sc.s;
+  }
+}
+
+// T consecutive tiles per wave, the next tile's code loads issued first.
+template <int FIN, int FOUT, int K, int U, int T>
 __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
                                                       float *__restrict__ so, uint64_t n,
                                                       uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
-  constexpr uint64_t kTileBlocks = kTile / kBlock;
   const uint32_t lane = lane_id();
-  const bool upper = lane >= 32;
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t = w0; t < full_tiles; t += nw) {
-    const uint64_t dw0 = t * (kTile / 4);
-    uint32_t w[K][U];
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    uint32_t cur[K][U];
+    load_codes<K, U>(P, t0, lane, cur);
 #pragma unroll
-    for (int p = 0; p < K; ++p)
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      uint32_t nxt[K][U];
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) load_codes<K, U>(P, t + 1, lane, nxt);
+      requant_tile<FIN, FOUT, K, U>(P, cur, qo, so, t, lane);
+      if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
-
-    float acc[U][4];
+        for (int p = 0; p < K; ++p)
 #pragma unroll
-    for (int p = 0; p < K; ++p) {
-      const float *sp = P.s[p] + t * kTileBlocks;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float s = upper ? sp[2 * u + 1] : sp[2 * u];
-        const f32x2 lo = dec2<FIN, false>(w[p][u]);
-        const f32x2 hi = dec2<FIN, true>(w[p][u]);
-        const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
-        if (p == 0) {
-          acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
-        } else {
-          acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
-          acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
-        }
+          for (int u = 0; u < U; ++u) cur[p][u] = nxt[p][u];
       }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t m = abs_bits(acc[u][0]);
-#pragma unroll
-      for (int j = 1; j < 4; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
-      const F32Scale sc = f32_block_scale<FOUT>(max_half32(m));
-      uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(acc[u][0], sc.s), f32_quot<FOUT>(acc[u][1], sc.s),
-                              f32_quot<FOUT>(acc[u][2], sc.s), f32_quot<FOUT>(acc[u][3], sc.s));
-      if (!sc.finite) c = 0x7F7F7F7Fu;
-      st(qo + dw0 + u * kWave + lane, c);
-      if ((lane & 31) == 0) so[t * kTileBlocks + 2 * u + (upper ? 1 : 0)] = sc.s;
     }
   }
   if (w0 == nw - 1)
@@ -295,9 +346,10 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
 template <int FIN, int FOUT, int K>
 hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
   constexpr int U = reduce_u<K>();
+  constexpr int T = FP8Q_RED_T;
   const uint64_t full = n / ((uint64_t)U * 256);
-  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U>), dim3(grid_for_tiles(full)), dim3(256), 0,
-                     stream, P, static_cast<uint32_t *>(qo), so, n, full);
+  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
+                     dim3(256), 0, stream, P, static_cast<uint32_t *>(qo), so, n, full);
   return hipGetLastError();
 }
 
@@ -347,7 +399,48 @@ __device__ void mx_reduce_tail(const MxPeerPtrs &P, void *__restrict__ y, uint64
   }
 }
 
+template <int K, int U>
+__device__ __forceinline__ void mx_load(const MxPeerPtrs &P, uint64_t t, uint32_t lane,
+                                        uint32_t (&w)[K][U], uint32_t (&c)[K][U]) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  const uint64_t dw0 = t * (kTile / 4);
+#pragma unroll
+  for (int p = 0; p < K; ++p)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+      c[p][u] = P.e[p][(t * kTile + (uint64_t)u * 256) / kMxBlock + lane / 8];
+    }
+}
+
 template <int K, int U, bool BF16>
+__device__ __forceinline__ void mx_reduce_tile(const uint32_t (&w)[K][U], const uint32_t (&c)[K][U],
+                                               void *__restrict__ y, uint64_t t, uint32_t lane) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  float acc[U][4];
+#pragma unroll
+  for (int p = 0; p < K; ++p)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = e8m0_value(c[p][u]);
+      const f32x2 lo = dec2<0, false>(w[p][u]);
+      const f32x2 hi = dec2<0, true>(w[p][u]);
+      const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
+      if (p == 0) {
+        acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
+      } else {
+        acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
+        acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
+      }
+    }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
+                 acc[u][3]);
+}
+
+// T consecutive tiles per wave, the next tile's loads issued first.
+template <int K, int U, int T, bool BF16>
 __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__restrict__ y,
                                                         uint64_t n, uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
@@ -355,37 +448,27 @@ __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__re
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t = w0; t < full_tiles; t += nw) {
-    const uint64_t dw0 = t * (kTile / 4);
-    uint32_t w[K][U];
-    uint32_t c[K][U];
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    uint32_t cw[K][U], cc[K][U];
+    mx_load<K, U>(P, t0, lane, cw, cc);
 #pragma unroll
-    for (int p = 0; p < K; ++p)
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      uint32_t nw_[K][U], nc[K][U];
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) mx_load<K, U>(P, t + 1, lane, nw_, nc);
+      mx_reduce_tile<K, U, BF16>(cw, cc, y, t, lane);
+      if (more) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
-        c[p][u] = P.e[p][(t * kTile + (uint64_t)u * 256) / kMxBlock + lane / 8];
+        for (int p = 0; p < K; ++p)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            cw[p][u] = nw_[p][u];
+            cc[p][u] = nc[p][u];
+          }
       }
-    float acc[U][4];
-#pragma unroll
-    for (int p = 0; p < K; ++p)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float s = e8m0_value(c[p][u]);
-        const f32x2 lo = dec2<0, false>(w[p][u]);
-        const f32x2 hi = dec2<0, true>(w[p][u]);
-        const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
-        if (p == 0) {
-          acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
-        } else {
-          acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
-          acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
-                   acc[u][3]);
+    }
   }
   if (w0 == nw - 1) mx_reduce_tail<K, BF16>(P, y, n, full_tiles * kTile);
 }
@@ -393,9 +476,10 @@ __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__re
 template <int K, bool BF16>
 hipError_t launch_mx_reduce_t(const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = reduce_u<K>();
+  constexpr int T = FP8Q_RED_T;
   const uint64_t full = n / ((uint64_t)U * 256);
-  hipLaunchKernelGGL((mx_reduce_kernel<K, U, BF16>), dim3(grid_for_tiles(full)), dim3(256), 0,
-                     stream, P, y, n, full);
+  hipLaunchKernelGGL((mx_reduce_kernel<K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
+                     dim3(256), 0, stream, P, y, n, full);
   return hipGetLastError();
 }
 

@@ -32,7 +32,11 @@ namespace {
 #ifndef FP8Q_MX_U
 #define FP8Q_MX_U 2
 #endif
+#ifndef FP8Q_MX_T
+#define FP8Q_MX_T 2
+#endif
 constexpr int kMxU = FP8Q_MX_U;              // 1 KiB loads in flight per wave per tile (<= 4)
+constexpr int kMxT = FP8Q_MX_T;              // consecutive tiles per wave (pipelined)
 static_assert(kMxU >= 1 && kMxU <= 4, "one E8M0 byte per lane covers at most 4 loads");
 
 struct MxScale {
@@ -69,33 +73,58 @@ __device__ __forceinline__ u32x2 mx_quant8(u32x4 v, const MxScale &m) {
 }
 
 template <int U>
+__device__ __forceinline__ void mx_tile(const u32x4 (&v)[U], u32x2 *__restrict__ q,
+                                       uint8_t *__restrict__ e8m0, uint64_t t, uint32_t lane) {
+  constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
+  constexpr uint64_t kBlocks = U * 16;             // 32-element blocks per tile
+  const uint32_t g = lane >> 2, c = lane & 3;
+  const uint64_t c0 = t * kChunks;
+  uint32_t codes[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const MxScale m = mx_scale(max_quad(amax_bits8(v[u])));
+    st(q + c0 + u * kWave + lane, mx_quant8(v[u], m));
+    codes[u] = m.code;
+  }
+  if (c < U) {
+    uint32_t code = codes[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) code = (c == (uint32_t)u) ? codes[u] : code;
+    e8m0[t * kBlocks + c * 16 + g] = (uint8_t)code;
+  }
+}
+
+// Each wave takes T consecutive tiles; the next tile's loads are issued
+// before the current tile's arithmetic.
+template <int U, int T>
 __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u32x2 *__restrict__ q,
                                                   uint8_t *__restrict__ e8m0, uint64_t nchunks,
                                                   uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
-  constexpr uint64_t kBlocks = U * 16;             // 32-element blocks per tile
   const uint32_t lane = lane_id();
-  const uint32_t g = lane >> 2, c = lane & 3;
+  const uint32_t c = lane & 3;
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t = w0; t < full_tiles; t += nw) {
-    const uint64_t c0 = t * kChunks;
-    u32x4 v[U];
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    u32x4 cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld(w + c0 + u * kWave + lane);
-    uint32_t codes[U];
+    for (int u = 0; u < U; ++u) cur[u] = ld(w + t0 * kChunks + u * kWave + lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const MxScale m = mx_scale(max_quad(amax_bits8(v[u])));
-      st(q + c0 + u * kWave + lane, mx_quant8(v[u], m));
-      codes[u] = m.code;
-    }
-    if (c < U) {
-      uint32_t code = codes[0];
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      u32x4 nxt[U];
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) {
 #pragma unroll
-      for (int u = 1; u < U; ++u) code = (c == (uint32_t)u) ? codes[u] : code;
-      e8m0[t * kBlocks + c * 16 + g] = (uint8_t)code;
+        for (int u = 0; u < U; ++u) nxt[u] = ld(w + (t + 1) * kChunks + u * kWave + lane);
+      }
+      mx_tile<U>(cur, q, e8m0, t, lane);
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      }
     }
   }
   // Tail: whole blocks only (the element count is a multiple of 32, so every
@@ -119,9 +148,11 @@ __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u
 hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0,
                                hipStream_t stream) {
   constexpr int U = kMxU;
+  constexpr int T = kMxT;
   const uint64_t nchunks = n / 8;
   const uint64_t full = nchunks / ((uint64_t)U * kWave);
-  hipLaunchKernelGGL((mx8_kernel<U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((mx8_kernel<U, T>), dim3(grid_for_tiles((full + T - 1) / T)), dim3(256), 0,
+                     stream,
                      static_cast<const u32x4 *>(w), static_cast<u32x2 *>(q),
                      static_cast<uint8_t *>(e8m0), nchunks, full);
   return hipGetLastError();

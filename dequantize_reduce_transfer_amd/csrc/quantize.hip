@@ -35,9 +35,13 @@ namespace fp8q {
 namespace {
 
 #ifndef FP8Q_QUANT_U
-#define FP8Q_QUANT_U 4
+#define FP8Q_QUANT_U 2
+#endif
+#ifndef FP8Q_QUANT_T
+#define FP8Q_QUANT_T 2
 #endif
 constexpr int kQuantU = FP8Q_QUANT_U;            // 1 KiB loads in flight per wave per tile
+constexpr int kQuantT = FP8Q_QUANT_T;            // consecutive tiles per wave
 
 struct BlockScale {
   float s;        // the stored scale (NaN for a non-finite block)
@@ -118,37 +122,63 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
   }
 }
 
+// One tile: quantize the U loaded chunks and store codes and scales.
 template <int FMT, int U>
+__device__ __forceinline__ void quantize_tile(const u32x4 (&v)[U], u32x2 *__restrict__ q,
+                                              float *__restrict__ scales, uint64_t t,
+                                              uint32_t lane) {
+  constexpr uint64_t kChunks = U * kWave;
+  constexpr uint64_t kBlocks = U * 4;
+  const uint32_t row = lane >> 4, col = lane & 15;
+  const uint64_t c0 = t * kChunks;
+  float sc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v[u])));
+    st(q + c0 + u * kWave + lane, quant8<FMT>(v[u], b));
+    sc[u] = b.s;
+  }
+  // block (u, row) of the tile is block u * 4 + row; lane (row, col = u)
+  // stores it, so one instruction writes the tile's 4U scales.
+  if (col < U) {
+    float s = sc[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) s = (col == (uint32_t)u) ? sc[u] : s;
+    scales[t * kBlocks + col * 4 + row] = s;
+  }
+}
+
+// Each wave takes T consecutive tiles; the next tile's loads are issued
+// before the current tile's arithmetic.
+template <int FMT, int U, int T>
 __global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__ x,
                                                        u32x2 *__restrict__ q,
                                                        float *__restrict__ scales, uint64_t n,
                                                        uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
-  constexpr uint64_t kBlocks = U * 4;              // blocks per tile
   const uint32_t lane = lane_id();
-  const uint32_t row = lane >> 4, col = lane & 15;
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t = w0; t < full_tiles; t += nw) {
-    const uint64_t c0 = t * kChunks;
-    u32x4 v[U];
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    u32x4 cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld(x + c0 + u * kWave + lane);
-    float sc[U];
+    for (int u = 0; u < U; ++u) cur[u] = ld(x + t0 * kChunks + u * kWave + lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const BlockScale b = block_scale<FMT>(max_row16(amax_bits8(v[u])));
-      st(q + c0 + u * kWave + lane, quant8<FMT>(v[u], b));
-      sc[u] = b.s;
-    }
-    // block (u, row) of the tile is block u * 4 + row; lane (row, col = u)
-    // stores it, so one instruction writes the tile's 16 scales (64 B).
-    if (col < U) {
-      float s = sc[0];
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      u32x4 nxt[U];
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) {
 #pragma unroll
-      for (int u = 1; u < U; ++u) s = (col == (uint32_t)u) ? sc[u] : s;
-      scales[t * kBlocks + col * 4 + row] = s;
+        for (int u = 0; u < U; ++u) nxt[u] = ld(x + (t + 1) * kChunks + u * kWave + lane);
+      }
+      quantize_tile<FMT, U>(cur, q, scales, t, lane);
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      }
     }
   }
   if (w0 == nw - 1)
@@ -159,9 +189,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__
 template <int FMT>
 hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
   constexpr int U = kQuantU;
+  constexpr int T = kQuantT;
   const uint64_t tile_elems = (uint64_t)U * kWave * 8;
   const uint64_t full = n / tile_elems;
-  hipLaunchKernelGGL((quantize_kernel<FMT, U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((quantize_kernel<FMT, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
+                     dim3(256), 0, stream,
                      static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, full);
   return hipGetLastError();
 }
@@ -184,15 +216,27 @@ __global__ __launch_bounds__(64) void tw_zero_kernel(uint32_t *slot) {
   if (threadIdx.x == 0) *slot = 0u;
 }
 
+constexpr int kAmaxU = 4;            // 16-byte loads in flight per thread
+
 __global__ __launch_bounds__(256) void tw_amax_kernel(const u32x4 *__restrict__ x, uint64_t n,
                                                       uint32_t *__restrict__ slot) {
   __shared__ uint32_t part[4];
   const uint64_t nch = n / 8;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * kAmaxU;
   uint32_t m = 0;
-  for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nch; c += stride) {
-    const uint32_t a = amax_bits8(ld(x + c));
-    m = m > a ? m : a;
+  for (uint64_t c0 = (uint64_t)blockIdx.x * blockDim.x * kAmaxU + threadIdx.x; c0 < nch;
+       c0 += stride) {
+    u32x4 v[kAmaxU];
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) {
+      const uint64_t c = c0 + (uint64_t)u * blockDim.x;
+      v[u] = c < nch ? ld(x + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxU; ++u) {
+      const uint32_t a = amax_bits8(v[u]);
+      m = m > a ? m : a;
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x < n - 8 * nch) {
     const uint32_t a = reinterpret_cast<const uint16_t *>(x)[8 * nch + threadIdx.x] & 0x7FFFu;
@@ -247,10 +291,10 @@ hipError_t launch_tw_t(const void *x, uint64_t n, void *q, float *scale, hipStre
   constexpr int U = kQuantU;
   uint32_t *slot = reinterpret_cast<uint32_t *>(scale);
   hipLaunchKernelGGL(tw_zero_kernel, dim3(1), dim3(64), 0, stream, slot);
-  // the amax pass only reads: a bounded grid-stride grid, so the atomics
-  // number a few thousand at most
-  uint64_t wgs = (n / 8 + 255) / 256;
-  if (wgs > 4096) wgs = 4096;
+  // the amax pass only reads: a bounded grid-stride grid (2048 workgroups
+  // measured best for pure reads), so the atomics number 2048 at most
+  uint64_t wgs = (n / 8 + 256 * kAmaxU - 1) / (256 * kAmaxU);
+  if (wgs > 2048) wgs = 2048;
   if (wgs < 1) wgs = 1;
   hipLaunchKernelGGL(tw_amax_kernel, dim3((uint32_t)wgs), dim3(256), 0, stream,
                      static_cast<const u32x4 *>(x), n, slot);

@@ -288,6 +288,29 @@ def next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out, reps=10):
     return res
 
 
+def k_sweep(torch, fq, q, s, dev, reps=10):
+    """Fused reduce into bf16 for k = 1, 2, 4, 8, 16 peers of 218,750,000
+    elements each: 16 distinct block-aligned slices of the quantized
+    gradient, so no peer is read twice."""
+    n = q.numel() // 16
+    stride = n // 128 * 128
+    qs = [q[p * stride:p * stride + n] for p in range(16)]
+    ss = [s[p * stride // 128:p * stride // 128 + fq.num_scales(n)] for p in range(16)]
+    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    out = []
+    for k in (1, 2, 4, 8, 16):
+        f = lambda k=k: fq.fp8q_dequant_reduce(qs[:k], ss[:k], fq.E4M3, out_dtype=torch.bfloat16,
+                                               out=y)
+        f()
+        ms = median_ms(torch, [f] * reps)
+        alg = reduce_bytes_per_elem(k, 2) * n
+        out.append({"k": k, "elements": n, "us": round(ms * 1e3, 2),
+                    "hbm_GBps": round(alg / ms / 1e6, 1),
+                    "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)})
+    del y
+    return out
+
+
 def stress_reduce(torch, fq, workloads, dev, reps=20):
     """k = 8 fused reduce into bf16 over the stress payload's shape: 8 peers x
     33,554,432 elements in 8 all-to-all chunks; "share" is one chunk (one
@@ -457,6 +480,8 @@ def main():
         del parts
         log("side figures: requantize, MXFP8 receiver, tensorwise")
         side.update(next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out))
+        log("side figures: peer-count sweep")
+        side["reduce_k_sweep_bf16"] = k_sweep(torch, fq, q, s, dev)
         log("side figures: payload sweep (e5m2) and stress reduce (bf16 out)")
         side["payload_sweep_e5m2"] = payload_sweep(torch, fq, workloads, dev)
         side["stress_reduce_k8_bf16"] = stress_reduce(torch, fq, workloads, dev)

@@ -35,7 +35,9 @@ MX_BLOCK = 32
 MAX_PEERS = 16
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfp8q.so")
+# FP8Q_LIB selects another build of the same library (e.g. one compiled with
+# a small grid cap to exercise the kernels' grid-stride loops in tests).
+LIB_PATH = os.environ.get("FP8Q_LIB") or os.path.join(_PKG, "libfp8q.so")
 _lib = None
 
 EXPORTS = ("fp8q_quantize", "fp8q_dequantize", "fp8q_dequant_reduce", "mx8_quantize",

@@ -21,7 +21,10 @@ constexpr int kMaxPeers = 16;
 // MI355X than a persistent grid, whose waves drift apart across the whole
 // buffer).  The cap keeps grid * 256 work-items inside the dispatch packet's
 // 32-bit range; beyond it the kernels' grid-stride loops take the rest.
-constexpr uint64_t kMaxWorkgroups = 1ull << 22;
+#ifndef FP8Q_MAX_WORKGROUPS
+#define FP8Q_MAX_WORKGROUPS (1ull << 22)
+#endif
+constexpr uint64_t kMaxWorkgroups = FP8Q_MAX_WORKGROUPS;
 
 inline uint32_t grid_for_tiles(uint64_t tiles) {
   uint64_t wgs = (tiles + 3) / 4;

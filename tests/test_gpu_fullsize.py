@@ -110,3 +110,38 @@ def test_stress_full_payload_bf16(fmt):
     torch.cuda.synchronize()
     want = oracle.dequant_reduce([a for a, _ in shards], [b for _, b in shards], fmt, out_bf16=True)
     assert_bf16_parity(host(y), want, "stress full")
+
+
+def test_quantize_and_reduce_beyond_2_pow_32_elements():
+    """n = 2^32 + 12345: element offsets past 32 bits, a ragged last block."""
+    dev = require_gpu()
+    n = (1 << 32) + 12345
+    x = workloads.segmented_gradient(n, seed=3, device=dev, segment=1 << 28)
+    q, s = fq.fp8q_quantize(x, fq.E4M3)
+    torch.cuda.synchronize()
+    nb = (n + 127) // 128
+    idx = _sample(nb - 1, 4096, seed=4, always=[(1 << 32) // 128 - 1, (1 << 32) // 128,
+                                                (1 << 32) // 128 + 1])
+    it = torch.from_numpy(idx).to(dev)
+    xb = host(x[:(nb - 1) * 128].view(-1, 128)[it])
+    q_o, s_o = oracle.quantize(xb.ravel(), fq.E4M3)
+    assert_bytes_equal(host(q[:(nb - 1) * 128].view(-1, 128)[it]).ravel(), q_o, "codes")
+    assert_bytes_equal(f32_bits(host(s[it])), f32_bits(s_o), "scales")
+    tail_x = workloads.bits(x[(nb - 1) * 128:])
+    tq, ts = oracle.quantize(tail_x, fq.E4M3)
+    assert_bytes_equal(host(q[(nb - 1) * 128:]), tq, "tail codes")
+    assert_bytes_equal(f32_bits(host(s[nb - 1:])), f32_bits(ts), "tail scale")
+    del x
+    # the same codes as two peers of a reduce into bf16 (past 2^32 elements)
+    y = fq.fp8q_dequant_reduce([q, q], [s, s], fq.E4M3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    eidx = np.unique(np.concatenate([np.random.default_rng(6).integers(0, n, 8192),
+                                     np.arange(n - 300, n), (1 << 32) + np.arange(-64, 64)]))
+    et = torch.from_numpy(eidx).to(dev)
+    bt = torch.from_numpy(eidx // 128).to(dev)
+    m = eidx.size
+    qq = np.zeros((m, 128), np.uint8)
+    qq[:, 0] = host(q[et])
+    sv = host(s[bt])
+    want = oracle.dequant_reduce([qq.ravel()] * 2, [sv] * 2, fq.E4M3, out_bf16=True)[::128]
+    assert_bf16_parity(host(y[et]), want, "reduce past 2^32")

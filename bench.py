@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,7 +45,7 @@ QUANT_BYTES_PER_ELEM = 2 + 1 + 4 / 128
 MX_BYTES_PER_ELEM = 2 + 1 + 1 / 32
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 QUANT_KERNEL_SRCS = [os.path.join(ROOT, "dequantize_reduce_transfer_amd", "csrc", f)
-                     for f in ("quantize.hip", "fp8q_device.h")]
+                     for f in ("quantize.hip", "fp8q_device.h", "launch.h")]
 
 
 def log(msg):
@@ -57,10 +58,15 @@ def reduce_bytes_per_elem(k, out_bytes):
 
 
 def source_digest(paths):
+    """SHA-256 of the kernel's sources with comments and whitespace removed,
+    so that only a change to the code itself invalidates measured counters."""
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -16,11 +16,14 @@
 // each peer's codes with 4-byte loads: one instruction reads 256 contiguous
 // bytes (4 codes per lane) and its output store writes 1 KiB (fp32) or 512 B
 // (bf16) contiguous.  A wave's tile is U such groups (U * 256 elements =
-// 2U blocks of 128); all k * U code loads are issued before any arithmetic.
-// Lanes 0-31 of a group share one block and lanes 32-63 the next, so a
-// peer's 2U scales of a tile are wave-uniform and come in through the scalar
-// cache.  Codes are decoded by the hardware packed FP8->fp32 conversion.
-// The dequantized values live only in registers.
+// 2U blocks of 128); all k * U code loads are issued before any arithmetic,
+// and each wave takes T consecutive tiles with the next tile's loads issued
+// before the current tile's arithmetic.  Lanes 0-31 of a group share one
+// block and lanes 32-63 the next, so a peer's 2U scales of a tile are
+// wave-uniform and come in through the scalar cache.  Codes are decoded by
+// the hardware packed FP8->fp32 conversion.  The dequantized values live
+// only in registers.  The file also holds the requantize variant and the
+// MXFP8 receiver, which share this mapping.
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -373,7 +376,8 @@ hipError_t dispatch_requant_k(int k, const PeerPtrs &P, uint64_t n, void *qo, fl
 // kernel runs over n = rows * K elements.  Each 4-code dword of a lane lies in
 // one 32-element block; its E8M0 byte is loaded per lane (8 lanes share it).
 // 2^(code-127) is built from bits: code 0 is the fp32 subnormal 2^-127 and
-// 0xFF is NaN.  Each product is exact; the sum is in peer order.
+// 0xFF is NaN.  Each product is exact (unless it overflows to +-inf, which
+// codes made by mx8_quantize never do); the sum is in peer order.
 
 struct MxPeerPtrs {
   const uint32_t *q[kMaxPeers];

@@ -179,7 +179,8 @@ FP8Q_API fp8q_status fp8q_dequant_reduce_requantize(const void *const *q_peers,
  * the receiver of the prequantized weights, whose E8M0 zero-scale clamp must
  * agree with the trainer's -- review "Verified clean").  Per element of the
  * [rows, K] codes, with the [rows, K/32] E8M0 bytes of mx8_quantize:
- *   d = dec_e4m3(q) * 2^(code - 127)      (exact in fp32; code 0xFF -> NaN)
+ *   d = dec_e4m3(q) * 2^(code - 127)      (exact in fp32 unless it overflows
+ *                                          to +-inf; code 0xFF -> NaN)
  * mx8_dequant_reduce sums k such shards in peer order, each addition rounded
  * to fp32; mx8_dequantize is k = 1.  Output fp32, or bf16 (RNE of the fp32).
  *   q / q_peers        [rows, K] uint8 E4M3 codes, device, 16-byte aligned

@@ -404,7 +404,8 @@ float oracle_e8m0_decode(uint8_t code)
 /* trainer's and the receiver's E8M0 zero-scale clamp agree ("perf: Reduce   */
 /* MXFP8 refit weight-transfer overheads", self-review, "Verified clean").   */
 /* The product is exact in fp32 (a 4-bit significand times a power of two   */
-/* no smaller than 2^-127).  READING: output fp32, or bf16 = RNE of it.      */
+/* no smaller than 2^-127) unless it overflows to +-inf, which codes made by */
+/* mx8_quantize never do.  READING: output fp32, or bf16 = RNE of it.        */
 /* ------------------------------------------------------------------------ */
 
 static float mx_value(const uint8_t *q, const uint8_t *e8m0, size_t K, size_t r, size_t c)

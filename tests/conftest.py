@@ -29,3 +29,18 @@ def _announce_gpu_case(request):
         sys.__stderr__.write("\n[gpu case] %s\n" % request.node.nodeid)
         sys.__stderr__.flush()
     yield
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_libraries():
+    """Build the HIP library (hipcc, no GPU needed) and the oracle if either is
+    missing, so a fresh tree can run the suite; nothing is rebuilt otherwise."""
+    import dequantize_reduce_transfer_amd as fq
+    import oracle
+
+    if not os.path.exists(fq.LIB_PATH) and not os.environ.get("FP8Q_LIB"):
+        from dequantize_reduce_transfer_amd import build as hip_build
+        sys.__stderr__.write("[conftest] building %s\n" % fq.LIB_PATH)
+        hip_build.build()
+    oracle.build(force=False)
+    yield

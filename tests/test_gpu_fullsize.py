@@ -145,3 +145,17 @@ def test_quantize_and_reduce_beyond_2_pow_32_elements():
     sv = host(s[bt])
     want = oracle.dequant_reduce([qq.ravel()] * 2, [sv] * 2, fq.E4M3, out_bf16=True)[::128]
     assert_bf16_parity(host(y[et]), want, "reduce past 2^32")
+
+
+def test_pi05_gradient_quantize_e5m2_full():
+    """The same 3.5e9-element gradient quantized to e5m2 (sampled blocks)."""
+    dev = require_gpu()
+    n = workloads.PI05_N
+    x = workloads.segmented_gradient(n, seed=0, device=dev)
+    q, s = fq.fp8q_quantize(x, fq.E5M2)
+    torch.cuda.synchronize()
+    idx = _sample(n // 128, 8192, seed=11)
+    it = torch.from_numpy(idx).to(dev)
+    q_o, s_o = oracle.quantize(host(x.view(-1, 128)[it]).ravel(), fq.E5M2)
+    assert_bytes_equal(host(q.view(-1, 128)[it]).ravel(), q_o, "e5m2 sampled codes")
+    assert_bytes_equal(f32_bits(host(s[it])), f32_bits(s_o), "e5m2 sampled scales")

@@ -180,3 +180,33 @@ def test_same_shard_twice_and_deterministic():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     want = oracle.dequant_reduce([host(q)] * 3, [host(s)] * 3, 0)
     assert_bytes_equal(f32_bits(host(a)), f32_bits(want), "same shard x3")
+
+
+def test_bf16_output_overflow_rounds_like_rne():
+    """fp32 results between bf16's largest finite value and fp32's: RNE sends
+    those at or above the midpoint to +-inf and the rest to +-max."""
+    dev = require_gpu()
+    bf16_max = float(np.array([0x7F7F0000], np.uint32).view(np.float32)[0])
+    mid = float(np.array([0x7F7F8000], np.uint32).view(np.float32)[0])
+    targets = np.array([bf16_max, np.nextafter(np.float32(mid), np.float32(0)), mid,
+                        np.nextafter(np.float32(mid), np.float32(np.inf)), 3.4e38], np.float32)
+    n = 128 * targets.size
+    q = np.zeros(n, np.uint8)
+    q[::128] = 0x38                    # e4m3 1.0: dec * s == s exactly
+    q[1::128] = 0xB8                   # -1.0
+    s = targets.copy()
+    for dt_bf in (False, True):
+        y = host(fq.fp8q_dequantize(dev_u8(q, dev), dev_f32(s, dev), 0,
+                                    out_dtype=torch.bfloat16 if dt_bf else torch.float32))
+        want = oracle.dequantize(q, s, 0, out_bf16=dt_bf)
+        if dt_bf:
+            assert_bf16_parity(y, want, "bf16 overflow")
+            assert (want[::128] == 0x7F80).sum() == 3 and (want[1::128] == 0xFF80).sum() == 3
+        else:
+            assert_bytes_equal(f32_bits(y), f32_bits(want), "f32")
+    # two peers whose fp32 sum overflows
+    big = np.full(1, 3.0e38, np.float32)
+    qq = np.zeros(128, np.uint8)
+    qq[0] = 0x38
+    y = host(fq.fp8q_dequant_reduce([dev_u8(qq, dev)] * 2, [dev_f32(big, dev)] * 2, 0))
+    assert np.isinf(y[0]) and y[0] > 0

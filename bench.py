@@ -20,8 +20,9 @@ kernels run on (torch's current stream); the roofline figure uses the
 dominant kernel (the 7 GB quantize) with its algorithmic HBM bytes
 (2 + 1 + 4/128 B per element).  Side figures (not in the step): the
 dequantize alone, and the naive dequantize-then-sum path that the fused
-kernel replaces.  The CPU baseline times the oracle (single-threaded C) on a
-bounded sample of the same workload.
+kernel replaces.  The CPU baseline times the oracle (plain C, run on
+independent block-aligned pieces from a pool of host threads, and again on
+one thread) on a bounded sample of the same workload.
 
 Prints exactly one JSON line on stdout; progress goes to stderr.
 """
@@ -110,39 +111,134 @@ class Timer:
         ev = self.pairs.get(name, [])
         return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev))
 
+    def spread_us(self, name):
+        """Median and minimum launch time in microseconds."""
+        v = sorted(a.elapsed_time(b) for a, b in self.pairs.get(name, []))
+        if not v:
+            return {}
+        return {"us_median": round(v[len(v) // 2] * 1e3, 2), "us_min": round(v[0] * 1e3, 2)}
+
     def reset(self):
         self.pairs = {}
 
 
-def cpu_baseline(x, peers, moe, frac, fmt):
-    """The oracle, as it stands, on the first `frac` of every input."""
-    import numpy as np
-    import oracle
+def _cpu_sample(x, peers, moe, frac):
+    """Host copies of the first `frac` of every input of the step."""
     from dequantize_reduce_transfer_amd import workloads
 
     n_q = int(x.numel() * frac) // 128 * 128
-    xs = workloads.bits(x[:n_q])
     n_r = int(peers[0][0].numel() * frac) // 128 * 128
-    qs = [q[:n_r].cpu().numpy() for q, _ in peers]
-    ss = [s[: n_r // 128].cpu().numpy() for _, s in peers]
     e_mx = max(1, int(moe["gate"].shape[0] * frac))
-    ws = {k: workloads.bits(v[:e_mx]).reshape((-1, v.shape[-1])) for k, v in moe.items()}
+    return {
+        "x": workloads.bits(x[:n_q]),
+        "qs": [q[:n_r].cpu().numpy() for q, _ in peers],
+        "ss": [s[: n_r // 128].cpu().numpy() for _, s in peers],
+        "ws": {k: workloads.bits(v[:e_mx]).reshape((-1, v.shape[-1])) for k, v in moe.items()},
+        "n_q": n_q, "n_r": n_r, "e_mx": e_mx,
+    }
+
+
+def _piece(total, parts, multiple):
+    """Piece length: total / parts rounded up to a multiple, at least one multiple."""
+    per = -(-total // parts)
+    return max(multiple, -(-per // multiple) * multiple)
+
+
+def _cpu_pieces(smp, fmt, threads):
+    """The sample's oracle calls, cut at block boundaries into about
+    4 * `threads` independent pieces (one piece each when threads == 1)."""
+    import oracle
+
+    parts = 1 if threads == 1 else 4 * threads
+    jobs = []
+    xq = smp["x"]
+    step = _piece(xq.size, parts, 128)
+    for a in range(0, xq.size, step):
+        jobs.append(lambda a=a, m=step: oracle.quantize(xq[a:a + m], fmt))
+    n_r = smp["n_r"]
+    step = _piece(n_r, parts, 128)
+    for a in range(0, n_r, step):
+        jobs.append(lambda a=a, m=step: oracle.dequant_reduce(
+            [q[a:a + m] for q in smp["qs"]], [s[a // 128:(a + m) // 128] for s in smp["ss"]], fmt))
+    for w in smp["ws"].values():
+        rows = w.shape[0]
+        step = _piece(rows, parts, 1)
+        for a in range(0, rows, step):
+            jobs.append(lambda w=w, a=a, m=step: oracle.mx8_quantize(w[a:a + m]))
+    return jobs
+
+
+def cpu_baseline(smp, fmt, threads):
+    """The oracle, as it stands, on the sample; with threads > 1 the same
+    calls run on independent block-aligned pieces from a thread pool (the
+    oracle's C calls release the GIL), as an OpenMP loop over blocks would."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    jobs = _cpu_pieces(smp, fmt, threads)
     t0 = time.perf_counter()
-    oracle.quantize(xs, fmt)
-    oracle.dequant_reduce(qs, ss, fmt)
-    for w in ws.values():
-        oracle.mx8_quantize(w)
+    if threads == 1:
+        for j in jobs:
+            j()
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            for f in [ex.submit(j) for j in jobs]:
+                f.result()
     dt = time.perf_counter() - t0
-    bf16_bytes = 2 * n_q + 2 * len(qs) * n_r + sum(2 * w.size for w in ws.values())
+    k = len(smp["qs"])
+    bf16_bytes = (2 * smp["n_q"] + 2 * k * smp["n_r"]
+                  + sum(2 * w.size for w in smp["ws"].values()))
     return {
         "value": round(bf16_bytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
         "sample": ("first %.4g of each input: quantize %d elements, dequant-reduce k=%d x %d "
-                   "elements, mx8 %d experts of each of 3 tensors; %.1f s of single-threaded "
-                   "oracle work" % (frac, n_q, len(qs), n_r, e_mx, dt)),
+                   "elements, mx8 %d experts of each of 3 tensors; %.2f s wall on %d host "
+                   "thread%s" % (smp["frac"], smp["n_q"], k, smp["n_r"], smp["e_mx"], dt, threads,
+                                 "" if threads == 1 else "s, block-aligned pieces")),
     }
+
+
+def host_threads():
+    """Host threads for the CPU baseline: the process's CPU set, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def device_info(torch, dev):
+    """What the figures were measured on.  Clock and memory attributes come
+    from hipDeviceGetAttribute in the HIP runtime this process already has
+    loaded (found in its memory map; no second copy is ever loaded)."""
+    p = torch.cuda.get_device_properties(dev)
+    info = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1), "hip_runtime": torch.version.hip,
+            "torch": torch.__version__}
+    try:
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path:
+            hip = ctypes.CDLL(path)
+            attrs = {"peak_sclk_MHz": 5, "mem_bus_width_bits": 59, "peak_mclk_MHz": 60}
+            for key, code in attrs.items():
+                v = ctypes.c_int(0)
+                if hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev.index or 0) == 0:
+                    info[key] = v.value // 1000 if key.endswith("MHz") else v.value
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    return info
 
 
 def median_ms(torch, fns):
@@ -188,11 +284,27 @@ def graph_ms(torch, fns, replays=5):
     return ms
 
 
+def host_latency_us(torch, fn, reps=50):
+    """Host enqueue -> completion: median wall time of one call (argument
+    checks, launch) followed by a device synchronize."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return round(ts[len(ts) // 2] * 1e6, 1)
+
+
 def payload_sweep(torch, fq, workloads, dev, reps=20):
     """e5m2 block quantize and k = 8 fused reduce (fp32 out) at the payload
     sizes of the sweep, each launch on a different window of 2 GiB pools so
     that the timed bytes come from HBM, not the 256 MB Infinity Cache.
-    Times are per launch of a graph of back-to-back launches."""
+    Times are per launch of a graph of back-to-back launches; payloads up to
+    4 MiB also get the host's enqueue-to-completion latency of one call."""
     n_pool = 1 << 30
     x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)
     q = torch.empty(n_pool, dtype=torch.uint8, device=dev)
@@ -221,13 +333,17 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
 
         qm = graph_ms(torch, [quant(i) for i in range(reps)])
         rm = graph_ms(torch, [red(i) for i in range(reps)])
-        out.append({"payload_bytes": nbytes, "elements": n,
-                    "quantize_us": round(qm * 1e3, 2),
-                    "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
-                    "quantize_bf16_equiv_GBps": round(2 * n / qm / 1e6, 1),
-                    "reduce_k8_us": round(rm * 1e3, 2),
-                    "reduce_k8_hbm_GBps": round(reduce_bytes_per_elem(8, 4) * n / rm / 1e6, 1),
-                    "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1)})
+        row = {"payload_bytes": nbytes, "elements": n,
+               "quantize_us": round(qm * 1e3, 2),
+               "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
+               "quantize_bf16_equiv_GBps": round(2 * n / qm / 1e6, 1),
+               "reduce_k8_us": round(rm * 1e3, 2),
+               "reduce_k8_hbm_GBps": round(reduce_bytes_per_elem(8, 4) * n / rm / 1e6, 1),
+               "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1)}
+        if nbytes <= 4 << 20:
+            row["quantize_host_latency_us"] = host_latency_us(torch, quant(0))
+            row["reduce_k8_host_latency_us"] = host_latency_us(torch, red(0))
+        out.append(row)
     del x, q, s, y
     return out
 
@@ -445,11 +561,13 @@ def main():
     ops["quantize_e4m3"] = {"elements": n, "us": round(q_ms * 1e3, 2),
                             "bf16_equiv_GBps": round(2 * n / q_ms / 1e6, 1),
                             "hbm_GBps": round(q_alg / q_ms / 1e6, 1),
-                            "frac_peak": round(q_alg / q_ms / 1e6 / HBM_PEAK_GBS, 4)}
+                            "frac_peak": round(q_alg / q_ms / 1e6 / HBM_PEAK_GBS, 4),
+                            **timer.spread_us("quantize")}
     ops["dequant_reduce_k8_f32"] = {"elements": n_shard, "us": round(r_ms * 1e3, 2),
                                     "bf16_equiv_GBps": round(2 * k * n_shard / r_ms / 1e6, 1),
                                     "hbm_GBps": round(r_alg / r_ms / 1e6, 1),
-                                    "frac_peak": round(r_alg / r_ms / 1e6 / HBM_PEAK_GBS, 4)}
+                                    "frac_peak": round(r_alg / r_ms / 1e6 / HBM_PEAK_GBS, 4),
+                                    **timer.spread_us("dequant_reduce")}
     mx_ms = 0.0
     for name, w in moe.items():
         ms = timer.mean_ms("mx8_" + name)
@@ -457,7 +575,8 @@ def main():
         alg = MX_BYTES_PER_ELEM * w.numel()
         ops["mx8_" + name] = {"elements": w.numel(), "us": round(ms * 1e3, 2),
                               "hbm_GBps": round(alg / ms / 1e6, 1),
-                              "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)}
+                              "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4),
+                              **timer.spread_us("mx8_" + name)}
     ops["mx8_layer"] = {"elements": n_mx, "us": round(mx_ms * 1e3, 2),
                         "hbm_GBps": round(MX_BYTES_PER_ELEM * n_mx / mx_ms / 1e6, 1),
                         "frac_peak": round(MX_BYTES_PER_ELEM * n_mx / mx_ms / 1e6 / HBM_PEAK_GBS, 4)}
@@ -529,12 +648,19 @@ def main():
         "roofline": roofline,
         "ops": ops,
         "side": side,
+        "env": device_info(torch, dev),
     }
 
     if not args.no_cpu_baseline:
-        log("CPU baseline: oracle on %.4g of the workload" % args.cpu_frac)
-        moe_cpu = {name: w for name, w in moe.items()}
-        out["cpu_baseline"] = cpu_baseline(x, peers, moe_cpu, args.cpu_frac, fmt)
+        smp = _cpu_sample(x, peers, moe, args.cpu_frac)
+        smp["frac"] = args.cpu_frac
+        threads = host_threads()
+        log("CPU baseline: oracle on %.4g of the workload, %d threads" % (args.cpu_frac, threads))
+        out["cpu_baseline"] = cpu_baseline(smp, fmt, threads)
+        if threads > 1:
+            log("CPU baseline: the same sample on one thread")
+            side["cpu_baseline_1_thread"] = cpu_baseline(smp, fmt, 1)
+        del smp
     else:
         out["cpu_baseline"] = None
 

@@ -20,7 +20,9 @@
 // and each wave takes T consecutive tiles with the next tile's loads issued
 // before the current tile's arithmetic.  Lanes 0-31 of a group share one
 // block and lanes 32-63 the next, so a peer's 2U scales of a tile are
-// wave-uniform and come in through the scalar cache.  Codes are decoded by
+// wave-uniform and come in through the scalar cache (or, for the peer counts
+// where scalar registers run short, through vector loads issued with the
+// codes).  Codes are decoded by
 // the hardware packed FP8->fp32 conversion.  The dequantized values live
 // only in registers.  The file also holds the requantize variant and the
 // MXFP8 receiver, which share this mapping.
@@ -36,8 +38,11 @@ namespace {
 #ifndef FP8Q_RED_U8
 #define FP8Q_RED_U8 2        // tile depth for 4 < k <= 8
 #endif
+#ifndef FP8Q_RED_U13
+#define FP8Q_RED_U13 1       // tile depth for 8 < k <= 13
+#endif
 #ifndef FP8Q_RED_U16
-#define FP8Q_RED_U16 1       // tile depth for 8 < k <= 16
+#define FP8Q_RED_U16 2       // tile depth for 13 < k <= 16
 #endif
 #ifndef FP8Q_RED_T
 #define FP8Q_RED_T 2         // consecutive tiles per wave (pipelined)
@@ -52,11 +57,14 @@ struct PartPtrs {
   const float *p[kMaxPeers];
 };
 
-// Codes in flight per wave: k * U * 256 B.  U shrinks as k grows so that the
-// 2U scales of every peer fit the scalar register file.
+// Codes in flight per wave: k * U * 256 B.  The depth per peer count was
+// chosen by measurement on MI355X (k-peer reduce of 218,750,000-element
+// shards): past 8 peers the scalar registers run short (2k peer pointers,
+// plus 2U scales per peer on the scalar path), and the best mix of tile
+// depth and scale path changes with k; see the vector-scale switch below.
 template <int K>
 constexpr int reduce_u() {
-  return K <= 4 ? FP8Q_RED_U4 : (K <= 8 ? FP8Q_RED_U8 : FP8Q_RED_U16);
+  return K <= 4 ? FP8Q_RED_U4 : (K <= 8 ? FP8Q_RED_U8 : (K <= 13 ? FP8Q_RED_U13 : FP8Q_RED_U16));
 }
 
 // Non-temporal code loads pay off when several peers stream in; the single
@@ -106,31 +114,73 @@ __device__ void reduce_tail(const PeerPtrs &P, void *__restrict__ y, uint64_t n,
   }
 }
 
-template <int K, int U>
-__device__ __forceinline__ void load_codes(const PeerPtrs &P, uint64_t t, uint32_t lane,
-                                           uint32_t (&w)[K][U]) {
+// Scale path.  By default a peer's 2U scales of a tile are wave-uniform
+// scalar loads.  In vector-scale mode they are vector loads issued together
+// with the codes (each lane fetches its own block's scale; the 32 lanes of
+// a block share one address), which frees scalar registers and starts the
+// scale fetch a tile ahead.  Measured on MI355X (218,750,000-element
+// shards, bf16 out): at U = 1, vector scales are 3-7% faster than the scalar
+// path for 9 and 10 peers, even at 11 and slower at 12 and 13; for 14..16
+// peers U = 2 on the scalar path is fastest (about 30% over U = 1, whose
+// scalar registers spill).  The requantize, whose block amax and scale math
+// need scalar registers too, is 4-8% faster with vector scales from 2 peers
+// up and about 30% faster at 16 peers with U = 2.
+#ifndef FP8Q_RED_VSCALE_MIN
+#define FP8Q_RED_VSCALE_MIN 9
+#endif
+#ifndef FP8Q_RED_VSCALE_MAX
+#define FP8Q_RED_VSCALE_MAX 11
+#endif
+#ifndef FP8Q_RQ_VSCALE_K
+#define FP8Q_RQ_VSCALE_K 2
+#endif
+template <int K>
+constexpr bool kRedVecScales = K >= FP8Q_RED_VSCALE_MIN && K <= FP8Q_RED_VSCALE_MAX;
+template <int K>
+constexpr bool kRqVecScales = K >= FP8Q_RQ_VSCALE_K;
+
+// One tile's inputs in registers: codes, and (vector-scale mode VS) scales.
+template <int K, int U, bool VS>
+struct TileIn {
+  uint32_t w[K][U];
+  float s[VS ? K : 1][VS ? U : 1];
+};
+
+template <int K, int U, bool VS>
+__device__ __forceinline__ void load_tile(const PeerPtrs &P, uint64_t t, uint32_t lane,
+                                          TileIn<K, U, VS> &in) {
   const uint64_t dw0 = t * ((uint64_t)U * 64);     // first code dword of tile t
 #pragma unroll
   for (int p = 0; p < K; ++p)
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+    for (int u = 0; u < U; ++u) in.w[p][u] = ld<uint32_t, kNtCodes<K>>(P.q[p] + dw0 + u * kWave + lane);
+  if constexpr (VS) {
+    const uint64_t b0 = t * (2u * U) + (lane >= 32 ? 1u : 0u);
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int u = 0; u < U; ++u) in.s[p][u] = ld<float, false>(P.s[p] + b0 + 2 * u);
+  }
 }
 
-template <int FMT, int K, int U, bool BF16>
-__device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const uint32_t (&w)[K][U],
-                                            void *__restrict__ y, uint64_t t, uint32_t lane) {
-  constexpr uint64_t kTile = (uint64_t)U * 256;    // elements per tile
-  constexpr uint64_t kTileBlocks = kTile / kBlock; // = 2U
+// The tile's k-peer sums: acc[u][j] is element 4 * lane + j of group u.
+template <int FMT, int K, int U, bool VS>
+__device__ __forceinline__ void sum_tile(const PeerPtrs &P, const TileIn<K, U, VS> &in, uint64_t t,
+                                         uint32_t lane, float (&acc)[U][4]) {
+  constexpr uint64_t kTileBlocks = 2 * U;
   const bool upper = lane >= 32;
-  float acc[U][4];
 #pragma unroll
   for (int p = 0; p < K; ++p) {
     const float *sp = P.s[p] + t * kTileBlocks;    // wave-uniform
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float s = upper ? sp[2 * u + 1] : sp[2 * u];
-      const f32x2 lo = dec2<FMT, false>(w[p][u]);
-      const f32x2 hi = dec2<FMT, true>(w[p][u]);
+      float s;
+      if constexpr (VS)
+        s = in.s[p][u];
+      else
+        s = upper ? sp[2 * u + 1] : sp[2 * u];
+      const f32x2 lo = dec2<FMT, false>(in.w[p][u]);
+      const f32x2 hi = dec2<FMT, true>(in.w[p][u]);
       const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
       if (p == 0) {
         acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
@@ -140,14 +190,22 @@ __device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const uint32_t (&
       }
     }
   }
+}
+
+template <int FMT, int K, int U, bool VS, bool BF16>
+__device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const TileIn<K, U, VS> &in,
+                                            void *__restrict__ y, uint64_t t, uint32_t lane) {
+  constexpr uint64_t kTile = (uint64_t)U * 256;    // elements per tile
+  float acc[U][4];
+  sum_tile<FMT, K, U, VS>(P, in, t, lane, acc);
 #pragma unroll
   for (int u = 0; u < U; ++u)
     store4<BF16>(y, t * kTile + (uint64_t)u * 256 + 4 * lane, acc[u][0], acc[u][1], acc[u][2],
                  acc[u][3]);
 }
 
-// Each wave takes T consecutive tiles; the next tile's code loads are
-// issued before the current tile's arithmetic.
+// Each wave takes T consecutive tiles; the next tile's loads are issued
+// before the current tile's arithmetic.
 template <int FMT, int K, int U, int T, bool BF16>
 __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restrict__ y, uint64_t n,
                                                      uint64_t full_tiles) {
@@ -156,23 +214,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
+  constexpr bool VS = kRedVecScales<K>;
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
-    uint32_t cur[K][U];
-    load_codes<K, U>(P, t0, lane, cur);
+    TileIn<K, U, VS> cur;
+    load_tile<K, U, VS>(P, t0, lane, cur);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       const uint64_t t = t0 + j;
       if (t >= full_tiles) break;
-      uint32_t nxt[K][U];
+      TileIn<K, U, VS> nxt;
       const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-      if (more) load_codes<K, U>(P, t + 1, lane, nxt);
-      reduce_tile<FMT, K, U, BF16>(P, cur, y, t, lane);
-      if (more) {
-#pragma unroll
-        for (int p = 0; p < K; ++p)
-#pragma unroll
-          for (int u = 0; u < U; ++u) cur[p][u] = nxt[p][u];
-      }
+      if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
+      reduce_tile<FMT, K, U, VS, BF16>(P, cur, y, t, lane);
+      if (more) cur = nxt;
     }
   }
   if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
@@ -273,8 +327,8 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
-template <int FIN, int FOUT, int K, int U>
-__device__ __forceinline__ void requant_tile(const PeerPtrs &P, const uint32_t (&w)[K][U],
+template <int FIN, int FOUT, int K, int U, bool VS>
+__device__ __forceinline__ void requant_tile(const PeerPtrs &P, const TileIn<K, U, VS> &in,
                                              uint32_t *__restrict__ qo, float *__restrict__ so,
                                              uint64_t t, uint32_t lane) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
@@ -282,23 +336,7 @@ __device__ __forceinline__ void requant_tile(const PeerPtrs &P, const uint32_t (
   const bool upper = lane >= 32;
   const uint64_t dw0 = t * (kTile / 4);
   float acc[U][4];
-#pragma unroll
-  for (int p = 0; p < K; ++p) {
-    const float *sp = P.s[p] + t * kTileBlocks;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float s = upper ? sp[2 * u + 1] : sp[2 * u];
-      const f32x2 lo = dec2<FIN, false>(w[p][u]);
-      const f32x2 hi = dec2<FIN, true>(w[p][u]);
-      const float d0 = lo[0] * s, d1 = lo[1] * s, d2 = hi[0] * s, d3 = hi[1] * s;
-      if (p == 0) {
-        acc[u][0] = d0; acc[u][1] = d1; acc[u][2] = d2; acc[u][3] = d3;
-      } else {
-        acc[u][0] = acc[u][0] + d0; acc[u][1] = acc[u][1] + d1;
-        acc[u][2] = acc[u][2] + d2; acc[u][3] = acc[u][3] + d3;
-      }
-    }
-  }
+  sum_tile<FIN, K, U, VS>(P, in, t, lane, acc);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     uint32_t m = abs_bits(acc[u][0]);
@@ -313,7 +351,7 @@ __device__ __forceinline__ void requant_tile(const PeerPtrs &P, const uint32_t (
   }
 }
 
-// T consecutive tiles per wave, the next tile's code loads issued first.
+// T consecutive tiles per wave, the next tile's loads issued first.
 template <int FIN, int FOUT, int K, int U, int T>
 __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
                                                       float *__restrict__ so, uint64_t n,
@@ -323,23 +361,19 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
+  constexpr bool VS = kRqVecScales<K>;
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
-    uint32_t cur[K][U];
-    load_codes<K, U>(P, t0, lane, cur);
+    TileIn<K, U, VS> cur;
+    load_tile<K, U, VS>(P, t0, lane, cur);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
       const uint64_t t = t0 + j;
       if (t >= full_tiles) break;
-      uint32_t nxt[K][U];
+      TileIn<K, U, VS> nxt;
       const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-      if (more) load_codes<K, U>(P, t + 1, lane, nxt);
-      requant_tile<FIN, FOUT, K, U>(P, cur, qo, so, t, lane);
-      if (more) {
-#pragma unroll
-        for (int p = 0; p < K; ++p)
-#pragma unroll
-          for (int u = 0; u < U; ++u) cur[p][u] = nxt[p][u];
-      }
+      if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
+      requant_tile<FIN, FOUT, K, U, VS>(P, cur, qo, so, t, lane);
+      if (more) cur = nxt;
     }
   }
   if (w0 == nw - 1)
@@ -477,9 +511,16 @@ __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__re
   if (w0 == nw - 1) mx_reduce_tail<K, BF16>(P, y, n, full_tiles * kTile);
 }
 
+// The MXFP8 receiver's tile depth: as the block-128 reduce up to 8 peers,
+// U = 1 beyond (its scales are always vector byte loads).
+template <int K>
+constexpr int mx_reduce_u() {
+  return K <= 8 ? reduce_u<K>() : 1;
+}
+
 template <int K, bool BF16>
 hipError_t launch_mx_reduce_t(const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
-  constexpr int U = reduce_u<K>();
+  constexpr int U = mx_reduce_u<K>();
   constexpr int T = FP8Q_RED_T;
   const uint64_t full = n / ((uint64_t)U * 256);
   hipLaunchKernelGGL((mx_reduce_kernel<K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),

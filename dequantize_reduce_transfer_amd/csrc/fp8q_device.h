@@ -150,9 +150,40 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Workgroup -> position in the buffer, XCD-aware.  The dispatcher deals
+// workgroups to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), so
+// with the identity every XCD streams every 8th workgroup-sized piece.  With
+// FP8Q_XCD_CHUNK = C > 0 each XCD takes C consecutive positions per round of
+// 8C workgroups instead, so each XCD's L2 sees long contiguous runs while the
+// chip's tiles in flight still form one window of 8C workgroups; C = -1 gives
+// each XCD one contiguous eighth of the grid; 0 is the identity.  Either
+// remap is a bijection on the whole rounds and the identity on the rest, so
+// the last workgroup stays last.  On MI355X, C = 64 measured about 3% faster
+// than the identity for the block quantize (1 MiB of bf16 per XCD run),
+// 1.5% for the MXFP8 quantize and 2.5% for the dequantize, with the k-peer
+// reduce unchanged; C = 4 and C = -1 were slower than the identity.
+#ifndef FP8Q_XCD_CHUNK
+#define FP8Q_XCD_CHUNK 64
+#endif
+__device__ __forceinline__ uint32_t block_position() {
+  const uint32_t b = blockIdx.x, g = gridDim.x;
+  if constexpr (FP8Q_XCD_CHUNK > 0) {
+    constexpr uint32_t kRound = 8u * FP8Q_XCD_CHUNK;
+    if (b >= g / kRound * kRound) return b;
+    const uint32_t m = b % kRound;
+    return b - m + (m % 8u) * FP8Q_XCD_CHUNK + m / 8u;
+  } else if constexpr (FP8Q_XCD_CHUNK < 0) {
+    const uint32_t whole = g / 8u * 8u;
+    if (b >= whole) return b;
+    return (b % 8u) * (whole / 8u) + b / 8u;
+  } else {
+    return b;
+  }
+}
+
 // Global wave index and wave count of a 1-D launch of 256-thread workgroups.
 __device__ __forceinline__ uint32_t wave_index() {
-  return uniform(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+  return uniform(block_position() * (blockDim.x / kWave) + threadIdx.x / kWave);
 }
 __device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (blockDim.x / kWave); }
 

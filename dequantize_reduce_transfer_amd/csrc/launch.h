@@ -17,9 +17,10 @@ namespace fp8q {
 constexpr int kMaxPeers = 16;
 
 // Grid size: one 4-wave workgroup per 4 tiles, so that the tiles in flight
-// at any moment form one contiguous window of the buffer (measured faster on
-// MI355X than a persistent grid, whose waves drift apart across the whole
-// buffer).  The cap keeps grid * 256 work-items inside the dispatch packet's
+// at any moment form one window of the buffer (measured faster on MI355X
+// than a persistent grid, whose waves drift apart across the whole buffer;
+// the workgroup -> position map inside the window is XCD-aware, see
+// block_position in fp8q_device.h).  The cap keeps grid * 256 work-items inside the dispatch packet's
 // 32-bit range; beyond it the kernels' grid-stride loops take the rest.
 #ifndef FP8Q_MAX_WORKGROUPS
 #define FP8Q_MAX_WORKGROUPS (1ull << 22)

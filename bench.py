@@ -348,6 +348,36 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
     return out
 
 
+def tiny_config(torch, fq, workloads, dev, reps=20):
+    """The 1,048,576-element tiny gradient: e4m3 quantize, dequantize to fp32
+    and the k = 4 reduce to fp32 (4 peers drawn with seeds 0-3).  At 2-8 MB
+    the data stays in the 256 MB Infinity Cache, so these are cache-hot
+    per-launch times in a graph of back-to-back launches, plus the host's
+    enqueue-to-completion latency of one call."""
+    xs = [workloads.tiny_gradient(p).to(dev) for p in range(4)]
+    peers = [fq.fp8q_quantize(x, fq.E4M3) for x in xs]
+    n = xs[0].numel()
+    q0, s0 = peers[0]
+    qo = torch.empty(n, dtype=torch.uint8, device=dev)
+    so = torch.empty(fq.num_scales(n), dtype=torch.float32, device=dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    ops = {
+        "quantize_e4m3": (lambda: fq.fp8q_quantize(xs[0], fq.E4M3, q_out=qo, scales_out=so),
+                          QUANT_BYTES_PER_ELEM),
+        "dequantize_f32": (lambda: fq.fp8q_dequantize(q0, s0, fq.E4M3, out=y),
+                           reduce_bytes_per_elem(1, 4)),
+        "reduce_k4_f32": (lambda: fq.fp8q_dequant_reduce([a for a, _ in peers],
+                                                         [b for _, b in peers], fq.E4M3, out=y),
+                          reduce_bytes_per_elem(4, 4)),
+    }
+    res = {"elements": n}
+    for name, (fn, bpe) in ops.items():
+        ms = graph_ms(torch, [fn] * reps)
+        res[name] = {"us": round(ms * 1e3, 2), "GBps": round(bpe * n / ms / 1e6, 1),
+                     "host_latency_us": host_latency_us(torch, fn)}
+    return res
+
+
 def next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out, reps=10):
     """The rows beyond the step, on the step's own data:
     - dequant-reduce -> requantize (e4m3 -> e4m3) of the 8 Pi0.5 shards;
@@ -607,6 +637,8 @@ def main():
         side.update(next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out))
         log("side figures: peer-count sweep")
         side["reduce_k_sweep_bf16"] = k_sweep(torch, fq, q, s, dev)
+        log("side figures: tiny gradient (cache-resident)")
+        side["tiny_gradient"] = tiny_config(torch, fq, workloads, dev)
         log("side figures: payload sweep (e5m2) and stress reduce (bf16 out)")
         side["payload_sweep_e5m2"] = payload_sweep(torch, fq, workloads, dev)
         side["stress_reduce_k8_bf16"] = stress_reduce(torch, fq, workloads, dev)

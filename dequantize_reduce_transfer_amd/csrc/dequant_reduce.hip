@@ -345,12 +345,13 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
+// One tile: sum, requantize, store the codes, and put the tile's 2U scales
+// at s_dst[0 .. 2U) in the workgroup's LDS staging array.
 template <int FIN, int FOUT, int K, int U, bool VS>
 __device__ __forceinline__ void requant_tile(const PeerPtrs &P, const TileIn<K, U, VS> &in,
-                                             uint32_t *__restrict__ qo, float *__restrict__ so,
+                                             uint32_t *__restrict__ qo, float *s_dst,
                                              uint64_t t, uint32_t lane) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
-  constexpr uint64_t kTileBlocks = kTile / kBlock;
   const bool upper = lane >= 32;
   const uint64_t dw0 = t * (kTile / 4);
   float acc[U][4];
@@ -365,34 +366,63 @@ __device__ __forceinline__ void requant_tile(const PeerPtrs &P, const TileIn<K, 
                             f32_quot<FOUT>(acc[u][2], sc.s), f32_quot<FOUT>(acc[u][3], sc.s));
     if (!sc.finite) c = 0x7F7F7F7Fu;
     st(qo + dw0 + u * kWave + lane, c);
-    if ((lane & 31) == 0) so[t * kTileBlocks + 2 * u + (upper ? 1 : 0)] = sc.s;
+    if ((lane & 31) == 0) s_dst[2 * u + (upper ? 1 : 0)] = sc.s;
   }
 }
 
-// T consecutive tiles per wave, the next tile's loads issued first.
+// A wave's T consecutive tiles [t0, t0 + T) (those below full_tiles), the
+// next tile's loads issued first; tile t0 + j puts its scales at
+// s_dst + 2U * j.
+template <int FIN, int FOUT, int K, int U, int T>
+__device__ __forceinline__ void requant_wave_tiles(const PeerPtrs &P, uint32_t *__restrict__ qo,
+                                                   float *s_dst, uint64_t t0, uint64_t full_tiles,
+                                                   uint32_t lane) {
+  constexpr bool VS = kRqVecScales<K>;
+  TileIn<K, U, VS> cur;
+  load_tile<K, U, VS>(P, t0, lane, cur);
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const uint64_t t = t0 + j;
+    if (t >= full_tiles) break;
+    TileIn<K, U, VS> nxt;
+    const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+    if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
+    requant_tile<FIN, FOUT, K, U, VS>(P, cur, qo, s_dst + 2 * U * j, t, lane);
+    if (more) cur = nxt;
+  }
+}
+
+// T consecutive tiles per wave.  The workgroup's 4T tiles stage their 8UT
+// scales in LDS, and they leave in one contiguous store rather than as 8UT
+// four-byte stores from different waves (measured 2.7% faster for k = 8).
 template <int FIN, int FOUT, int K, int U, int T>
 __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
                                                       float *__restrict__ so, uint64_t n,
                                                       uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
+  constexpr uint32_t kTileBlocks = 2 * U;
+  constexpr uint32_t kWgTiles = 4 * T;             // 4 waves per workgroup
   const uint32_t lane = lane_id();
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  constexpr bool VS = kRqVecScales<K>;
-  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
-    TileIn<K, U, VS> cur;
-    load_tile<K, U, VS>(P, t0, lane, cur);
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      const uint64_t t = t0 + j;
-      if (t >= full_tiles) break;
-      TileIn<K, U, VS> nxt;
-      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-      if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
-      requant_tile<FIN, FOUT, K, U, VS>(P, cur, qo, so, t, lane);
-      if (more) cur = nxt;
-    }
+  __shared__ float wg_scales[kWgTiles * kTileBlocks];
+  const uint32_t wid = uniform(threadIdx.x / kWave);
+  const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
+  // Same trip count for every wave of the workgroup: the barriers are
+  // reached by all of them.
+  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
+       base += stride) {
+    const uint64_t t0 = base + (uint64_t)wid * T;
+    if (t0 < full_tiles)
+      requant_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
+                                             full_tiles, lane);
+    __syncthreads();
+    const uint64_t left = (full_tiles - base) * kTileBlocks;
+    const uint32_t nb = left < (uint64_t)(kWgTiles * kTileBlocks) ? (uint32_t)left
+                                                                 : kWgTiles * kTileBlocks;
+    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) so[base * kTileBlocks + i] = wg_scales[i];
+    if (base + stride < full_tiles) __syncthreads();   // before the next round reuses it
   }
   if (w0 == nw - 1)
     requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);

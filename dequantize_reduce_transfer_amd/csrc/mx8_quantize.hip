@@ -74,11 +74,14 @@ __device__ __forceinline__ u32x2 mx_quant8(u32x4 v, const MxScale &m) {
   return r;
 }
 
+constexpr int kWgWaves = 4;                      // waves per 256-thread workgroup
+
+// One tile: quantize, store the codes, and put the tile's 16U E8M0 bytes at
+// e_dst[0 .. 16U) in the workgroup's LDS staging array.
 template <int U>
 __device__ __forceinline__ void mx_tile(const u32x4 (&v)[U], u32x2 *__restrict__ q,
-                                       uint8_t *__restrict__ e8m0, uint64_t t, uint32_t lane) {
+                                       uint8_t *e_dst, uint64_t t, uint32_t lane) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
-  constexpr uint64_t kBlocks = U * 16;             // 32-element blocks per tile
   const uint32_t g = lane >> 2, c = lane & 3;
   const uint64_t c0 = t * kChunks;
   uint32_t codes[U];
@@ -92,42 +95,79 @@ __device__ __forceinline__ void mx_tile(const u32x4 (&v)[U], u32x2 *__restrict__
     uint32_t code = codes[0];
 #pragma unroll
     for (int u = 1; u < U; ++u) code = (c == (uint32_t)u) ? codes[u] : code;
-    e8m0[t * kBlocks + c * 16 + g] = (uint8_t)code;
+    e_dst[c * 16 + g] = (uint8_t)code;
   }
 }
 
-// Each wave takes T consecutive tiles; the next tile's loads are issued
-// before the current tile's arithmetic.
+// A wave's T consecutive tiles [t0, t0 + T) (those below full_tiles), the
+// next tile's loads issued before the current tile's arithmetic; tile
+// t0 + j puts its scale bytes at e_dst + 16U * j.
+template <int U, int T>
+__device__ __forceinline__ void mx_wave_tiles(const u32x4 *__restrict__ w, u32x2 *__restrict__ q,
+                                              uint8_t *e_dst, uint64_t t0, uint64_t full_tiles,
+                                              uint32_t lane) {
+  constexpr uint64_t kChunks = U * kWave;
+  u32x4 cur[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = ld(w + t0 * kChunks + u * kWave + lane);
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const uint64_t t = t0 + j;
+    if (t >= full_tiles) break;
+    u32x4 nxt[U];
+    const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u] = ld(w + (t + 1) * kChunks + u * kWave + lane);
+    }
+    mx_tile<U>(cur, q, e_dst + 16 * U * j, t, lane);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+  }
+}
+
+// Each wave takes T consecutive tiles.  The workgroup's 4T tiles stage
+// their E8M0 bytes in LDS, and they leave in one contiguous store (whole
+// 128-byte lines: 4-byte stores when the scale pointer allows, else bytes)
+// rather than as 4T partial-line byte stores from different waves.
 template <int U, int T>
 __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u32x2 *__restrict__ q,
                                                   uint8_t *__restrict__ e8m0, uint64_t nchunks,
                                                   uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
+  constexpr uint32_t kTileBytes = 16 * U;          // E8M0 bytes per tile
+  constexpr uint32_t kWgTiles = kWgWaves * T;
   const uint32_t lane = lane_id();
   const uint32_t c = lane & 3;
   const uint64_t nw = wave_count();
   const uint64_t w0 = wave_index();
 
-  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
-    u32x4 cur[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = ld(w + t0 * kChunks + u * kWave + lane);
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      const uint64_t t = t0 + j;
-      if (t >= full_tiles) break;
-      u32x4 nxt[U];
-      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) nxt[u] = ld(w + (t + 1) * kChunks + u * kWave + lane);
-      }
-      mx_tile<U>(cur, q, e8m0, t, lane);
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-      }
+  __shared__ uint32_t wg_e8m0[kWgTiles * kTileBytes / 4];
+  uint8_t *stage = reinterpret_cast<uint8_t *>(wg_e8m0);
+  const uint32_t wid = uniform(threadIdx.x / kWave);
+  const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
+  const bool words = (reinterpret_cast<uintptr_t>(e8m0) & 3u) == 0;
+  // Same trip count for every wave of the workgroup: the barriers are
+  // reached by all of them.
+  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
+       base += stride) {
+    const uint64_t t0 = base + (uint64_t)wid * T;
+    if (t0 < full_tiles)
+      mx_wave_tiles<U, T>(w, q, stage + wid * T * kTileBytes, t0, full_tiles, lane);
+    __syncthreads();
+    const uint64_t left = (full_tiles - base) * kTileBytes;
+    const uint32_t nb = left < (uint64_t)(kWgTiles * kTileBytes) ? (uint32_t)left
+                                                                : kWgTiles * kTileBytes;
+    uint8_t *dst = e8m0 + base * kTileBytes;
+    if (words) {
+      for (uint32_t i = threadIdx.x; i < nb / 4; i += blockDim.x)
+        reinterpret_cast<uint32_t *>(dst)[i] = wg_e8m0[i];
+    } else {
+      for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) dst[i] = stage[i];
     }
+    if (base + stride < full_tiles) __syncthreads();   // before the next round reuses it
   }
   // Tail: whole blocks only (the element count is a multiple of 32, so every
   // quad of chunks is either entirely present or entirely absent).

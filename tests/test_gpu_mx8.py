@@ -92,3 +92,22 @@ def test_zero_tiny_and_nonfinite_blocks():
     w[3, 65] = 0x43E0             # 448
     w[3, 96] = 0x43F0             # 480: saturates
     _check(w, dev, "special blocks")
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3, 4])
+def test_scale_pointer_at_any_byte_offset(offset):
+    """E8M0 output at a pointer that is not 4-byte aligned (the kernel then
+    writes its staged scale bytes one by one); bytes around it untouched."""
+    dev = require_gpu()
+    rows, K = 300, 2048                          # several workgroups of scale bytes
+    w = workloads.kaiming_uniform((rows, K), seed=30 + offset, device=dev)
+    ne = rows * K // 32
+    buf = torch.full((ne + 8,), 0xA5, dtype=torch.uint8, device=dev)
+    e = buf[offset:offset + ne]
+    q, _ = fq.mx8_quantize(w, e8m0_out=e)
+    torch.cuda.synchronize()
+    q_o, e_o = oracle.mx8_quantize(workloads.bits(w).reshape(rows, K))
+    assert_bytes_equal(host(q).ravel(), q_o.ravel(), "codes")
+    b = host(buf)
+    assert_bytes_equal(b[offset:offset + ne], e_o.ravel(), "e8m0")
+    assert np.all(b[:offset] == 0xA5) and np.all(b[offset + ne:] == 0xA5)

@@ -99,6 +99,17 @@ def _check(status: int, what: str) -> None:
         raise Fp8qError(status, "%s: %s" % (what, fp8q_status_str(status)))
 
 
+def _run(what: str, tensors, fn, *args) -> None:
+    """Call a C entry point with every tensor on one GPU, that GPU current
+    (the library launches on the current HIP device)."""
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError("%s: all tensors must be on %s, got one on %s" % (what, dev, t.device))
+    with torch.cuda.device(dev):
+        _check(fn(*args), what)
+
+
 def _stream(t: torch.Tensor, stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
@@ -151,8 +162,8 @@ def fp8q_quantize(x: torch.Tensor, fmt: int = E4M3, q_out: Optional[torch.Tensor
     _need(scales_out, torch.float32, "scales_out")
     if q_out.numel() != n or scales_out.numel() != num_scales(n):
         raise ValueError("q_out must hold n codes and scales_out ceil(n/128) scales")
-    _check(lib().fp8q_quantize(x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(),
-                               scales_out.data_ptr(), _stream(x, stream)), "fp8q_quantize")
+    _run("fp8q_quantize", [x, q_out, scales_out], lib().fp8q_quantize, x.data_ptr(), n,
+         _fmt(fmt), q_out.data_ptr(), scales_out.data_ptr(), _stream(x, stream))
     return q_out, scales_out
 
 
@@ -169,8 +180,8 @@ def fp8q_dequantize(q: torch.Tensor, scales: torch.Tensor, fmt: int = E4M3,
     _need(out, out_dtype, "out")
     if out.numel() != n:
         raise ValueError("out must hold n values")
-    _check(lib().fp8q_dequantize(q.data_ptr(), scales.data_ptr(), n, _fmt(fmt), out.data_ptr(),
-                                 _out_code(out_dtype), _stream(q, stream)), "fp8q_dequantize")
+    _run("fp8q_dequantize", [q, scales, out], lib().fp8q_dequantize, q.data_ptr(),
+         scales.data_ptr(), n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(q, stream))
     return out
 
 
@@ -194,9 +205,8 @@ def fp8q_dequant_reduce(qs: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
     _need(out, out_dtype, "out")
     if out.numel() != n:
         raise ValueError("out must hold n values")
-    _check(lib().fp8q_dequant_reduce(_ptrs(qs), _ptrs(scales), k, n, _fmt(fmt), out.data_ptr(),
-                                     _out_code(out_dtype), _stream(qs[0], stream)),
-           "fp8q_dequant_reduce")
+    _run("fp8q_dequant_reduce", [*qs, *scales, out], lib().fp8q_dequant_reduce, _ptrs(qs),
+         _ptrs(scales), k, n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream))
     return out
 
 
@@ -218,8 +228,8 @@ def mx8_quantize(w: torch.Tensor, q_out: Optional[torch.Tensor] = None,
     _need(e8m0_out, torch.uint8, "e8m0_out")
     if q_out.numel() != w.numel() or e8m0_out.numel() != rows * (K // MX_BLOCK):
         raise ValueError("output sizes do not match w")
-    _check(lib().mx8_quantize(w.data_ptr(), rows, K, q_out.data_ptr(), e8m0_out.data_ptr(),
-                              _stream(w, stream)), "mx8_quantize")
+    _run("mx8_quantize", [w, q_out, e8m0_out], lib().mx8_quantize, w.data_ptr(), rows, K,
+         q_out.data_ptr(), e8m0_out.data_ptr(), _stream(w, stream))
     return q_out, e8m0_out
 
 
@@ -237,8 +247,10 @@ def fp8q_sum_f32(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
     if out is None:
         out = torch.empty(n, dtype=out_dtype, device=parts[0].device)
     _need(out, out_dtype, "out")
-    _check(lib().fp8q_sum_f32(_ptrs(parts), k, n, out.data_ptr(), _out_code(out_dtype),
-                              _stream(parts[0], stream)), "fp8q_sum_f32")
+    if out.numel() != n:
+        raise ValueError("out must hold n values")
+    _run("fp8q_sum_f32", [*parts, out], lib().fp8q_sum_f32, _ptrs(parts), k, n, out.data_ptr(),
+         _out_code(out_dtype), _stream(parts[0], stream))
     return out
 
 
@@ -266,10 +278,9 @@ def fp8q_dequant_reduce_requantize(qs: Sequence[torch.Tensor], scales: Sequence[
     _need(scales_out, torch.float32, "scales_out")
     if q_out.numel() != n or scales_out.numel() != num_scales(n):
         raise ValueError("q_out must hold n codes and scales_out ceil(n/128) scales")
-    _check(lib().fp8q_dequant_reduce_requantize(_ptrs(qs), _ptrs(scales), k, n, _fmt(fmt_in),
-                                                _fmt(fmt_out), q_out.data_ptr(),
-                                                scales_out.data_ptr(), _stream(qs[0], stream)),
-           "fp8q_dequant_reduce_requantize")
+    _run("fp8q_dequant_reduce_requantize", [*qs, *scales, q_out, scales_out],
+         lib().fp8q_dequant_reduce_requantize, _ptrs(qs), _ptrs(scales), k, n, _fmt(fmt_in),
+         _fmt(fmt_out), q_out.data_ptr(), scales_out.data_ptr(), _stream(qs[0], stream))
     return q_out, scales_out
 
 
@@ -294,9 +305,8 @@ def mx8_dequant_reduce(qs: Sequence[torch.Tensor], e8m0s: Sequence[torch.Tensor]
     _need(out, out_dtype, "out")
     if out.numel() != qs[0].numel():
         raise ValueError("out must hold rows * K values")
-    _check(lib().mx8_dequant_reduce(_ptrs(qs), _ptrs(e8m0s), k, rows, K, out.data_ptr(),
-                                    _out_code(out_dtype), _stream(qs[0], stream)),
-           "mx8_dequant_reduce")
+    _run("mx8_dequant_reduce", [*qs, *e8m0s, out], lib().mx8_dequant_reduce, _ptrs(qs),
+         _ptrs(e8m0s), k, rows, K, out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream))
     return out
 
 
@@ -316,8 +326,8 @@ def mx8_dequantize(q: torch.Tensor, e8m0: torch.Tensor, out_dtype=torch.float32,
     _need(out, out_dtype, "out")
     if out.numel() != q.numel():
         raise ValueError("out must hold rows * K values")
-    _check(lib().mx8_dequantize(q.data_ptr(), e8m0.data_ptr(), rows, K, out.data_ptr(),
-                                _out_code(out_dtype), _stream(q, stream)), "mx8_dequantize")
+    _run("mx8_dequantize", [q, e8m0, out], lib().mx8_dequantize, q.data_ptr(), e8m0.data_ptr(),
+         rows, K, out.data_ptr(), _out_code(out_dtype), _stream(q, stream))
     return out
 
 
@@ -334,7 +344,6 @@ def fp8q_quantize_tensorwise(x: torch.Tensor, fmt: int = E4M3, q_out: Optional[t
     _need(scale_out, torch.float32, "scale_out")
     if q_out.numel() != n or scale_out.numel() != 1:
         raise ValueError("q_out must hold n codes and scale_out one scale")
-    _check(lib().fp8q_quantize_tensorwise(x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(),
-                                          scale_out.data_ptr(), _stream(x, stream)),
-           "fp8q_quantize_tensorwise")
+    _run("fp8q_quantize_tensorwise", [x, q_out, scale_out], lib().fp8q_quantize_tensorwise,
+         x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(), scale_out.data_ptr(), _stream(x, stream))
     return q_out, scale_out

@@ -61,3 +61,24 @@ def test_rejected_calls_write_nothing():
     assert L.fp8q_quantize_tensorwise(y.data_ptr(), n, 0, qo.data_ptr(), so.data_ptr() + 2, None) == 3
     torch.cuda.synchronize()
     assert torch.all(y == 7.0) and torch.all(qo == 0x11) and torch.all(so == 3.0)
+
+
+def test_binding_rejects_wrong_output_sizes():
+    """Output tensors of the wrong size are refused before any launch."""
+    dev = require_gpu()
+    n = 4096
+    parts = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(3)]
+    small = torch.full((n - 1,), 5.0, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        fq.fp8q_sum_f32(parts, out=small)
+    q = torch.zeros(n, dtype=torch.uint8, device=dev)
+    s = torch.ones(n // 128, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        fq.fp8q_dequant_reduce([q, q], [s, s], 0, out=small)
+    with pytest.raises(ValueError):
+        fq.fp8q_dequantize(q, s[:-1], 0)
+    x = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        fq.fp8q_quantize(x, 0, q_out=q[:-16])
+    torch.cuda.synchronize()
+    assert torch.all(small == 5.0)

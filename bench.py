@@ -632,6 +632,17 @@ def main():
                                   "frac_peak": round(d_alg / d_ms / 1e6 / HBM_PEAK_GBS, 4)}
         side["naive_dequant_then_sum_k8_us"] = round(naive_ms * 1e3, 2)
         side["fused_speedup_vs_naive"] = round(naive_ms / r_ms, 2)
+        log("side figures: the step captured in a HIP graph")
+
+        def plain_step():
+            fq.fp8q_quantize(x, fmt, q_out=q, scales_out=s)
+            fq.fp8q_dequant_reduce(qs, ss, fmt, out=y)
+            for name, w in moe.items():
+                fq.mx8_quantize(w, q_out=mx_out[name][0], e8m0_out=mx_out[name][1])
+        g_ms = graph_ms(torch, [plain_step], replays=10)
+        side["step_in_hip_graph"] = {"ms_per_step": round(g_ms, 4),
+                                     "bf16_equiv_GBps": round(bf16_bytes_step / g_ms / 1e6, 1),
+                                     "eager_ms_per_step": round(ms_step, 4)}
         del parts
         log("side figures: requantize, MXFP8 receiver, tensorwise")
         side.update(next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out))

@@ -241,7 +241,13 @@ __global__ __launch_bounds__(64) void tw_zero_kernel(uint32_t *slot) {
   if (threadIdx.x == 0) *slot = 0u;
 }
 
-constexpr int kAmaxU = 4;            // 16-byte loads in flight per thread
+#ifndef FP8Q_AMAX_U
+#define FP8Q_AMAX_U 4
+#endif
+#ifndef FP8Q_AMAX_WGS
+#define FP8Q_AMAX_WGS 512
+#endif
+constexpr int kAmaxU = FP8Q_AMAX_U;  // 16-byte loads in flight per thread
 
 __global__ __launch_bounds__(256) void tw_amax_kernel(const u32x4 *__restrict__ x, uint64_t n,
                                                       uint32_t *__restrict__ slot) {
@@ -316,10 +322,12 @@ hipError_t launch_tw_t(const void *x, uint64_t n, void *q, float *scale, hipStre
   constexpr int U = kQuantU;
   uint32_t *slot = reinterpret_cast<uint32_t *>(scale);
   hipLaunchKernelGGL(tw_zero_kernel, dim3(1), dim3(64), 0, stream, slot);
-  // the amax pass only reads: a bounded grid-stride grid (2048 workgroups
-  // measured best for pure reads), so the atomics number 2048 at most
+  // the amax pass only reads: a bounded grid-stride grid, so the atomics
+  // number FP8Q_AMAX_WGS at most.  On MI355X (7 GB of bf16) 512-1024
+  // workgroups read at ~7.0 TB/s, 4.5% faster than 2048 and 15% faster
+  // than 256.
   uint64_t wgs = (n / 8 + 256 * kAmaxU - 1) / (256 * kAmaxU);
-  if (wgs > 2048) wgs = 2048;
+  if (wgs > FP8Q_AMAX_WGS) wgs = FP8Q_AMAX_WGS;
   if (wgs < 1) wgs = 1;
   hipLaunchKernelGGL(tw_amax_kernel, dim3((uint32_t)wgs), dim3(256), 0, stream,
                      static_cast<const u32x4 *>(x), n, slot);

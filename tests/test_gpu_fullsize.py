@@ -4,6 +4,7 @@ cannot redo the whole output in seconds, sampled blocks / elements are
 checked exactly: every block (and every reduced element) depends only on its
 own inputs, so a sample is checked by running the oracle on just those
 inputs."""
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -159,3 +160,113 @@ def test_pi05_gradient_quantize_e5m2_full():
     q_o, s_o = oracle.quantize(host(x.view(-1, 128)[it]).ravel(), fq.E5M2)
     assert_bytes_equal(host(q.view(-1, 128)[it]).ravel(), q_o, "e5m2 sampled codes")
     assert_bytes_equal(f32_bits(host(s[it])), f32_bits(s_o), "e5m2 sampled scales")
+
+
+# ---------------------------------------------------------------------------
+# The same full-size outputs checked in full by the oracle itself, streamed:
+# block-aligned chunks are copied to the host and the oracle runs on them
+# from a pool of host threads (its C calls release the GIL).  Every block and
+# every reduced element depends only on its own inputs, so a chunked oracle
+# run equals one run over the whole tensor.
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def _pieces(a, b, parts, multiple):
+    step = max(multiple, -(-(-(-(b - a) // parts)) // multiple) * multiple)
+    return [(i, min(b, i + step)) for i in range(a, b, step)]
+
+
+@pytest.mark.parametrize("fmt", [fq.E4M3, fq.E5M2])
+def test_pi05_gradient_quantize_every_block_by_the_oracle(fmt):
+    """All 27,343,750 blocks of the 3.5e9-element gradient against the oracle."""
+    dev = require_gpu()
+    n = workloads.PI05_N
+    x = workloads.segmented_gradient(n, seed=0, device=dev)
+    q, s = fq.fp8q_quantize(x, fmt)
+    torch.cuda.synchronize()
+    batch = 1 << 28
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        for a in range(0, n, batch):
+            b = min(n, a + batch)
+            xb = workloads.bits(x[a:b])
+            qb, sb = host(q[a:b]), host(s[a // 128:(b + 127) // 128])
+            parts = _pieces(0, b - a, 4 * _threads(), 128)
+            outs = list(ex.map(lambda p: oracle.quantize(xb[p[0]:p[1]], fmt), parts))
+            for (i, j), (q_o, s_o) in zip(parts, outs):
+                assert_bytes_equal(qb[i:j], q_o, "codes [%d, %d)" % (a + i, a + j))
+                assert_bytes_equal(f32_bits(sb[i // 128:(j + 127) // 128]), f32_bits(s_o),
+                                   "scales [%d, %d)" % (a + i, a + j))
+
+
+def test_pi05_peer_shard_quantize_tail_and_canaries_by_the_oracle():
+    """One 437,500,000-element peer shard (a 96-element last block) written
+    into larger buffers: every code and scale against the oracle, and the
+    canaries past the end untouched."""
+    dev = require_gpu()
+    n = workloads.PI05_SHARD_N
+    x = workloads.pi05_peer_shard(3, n, device=dev)
+    nb = fq.num_scales(n)
+    qbuf = torch.full((n + 4096,), 0x5A, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((nb + 64,), -7.0, dtype=torch.float32, device=dev)
+    fq.fp8q_quantize(x, fq.E4M3, q_out=qbuf[:n], scales_out=sbuf[:nb])
+    torch.cuda.synchronize()
+    xb = workloads.bits(x)
+    parts = _pieces(0, n, 4 * _threads(), 128)
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        outs = list(ex.map(lambda p: oracle.quantize(xb[p[0]:p[1]], fq.E4M3), parts))
+    qh, sh = host(qbuf), host(sbuf)
+    assert_bytes_equal(qh[:n], np.concatenate([o[0] for o in outs]), "codes")
+    assert_bytes_equal(f32_bits(sh[:nb]), f32_bits(np.concatenate([o[1] for o in outs])), "scales")
+    assert np.all(qh[n:] == 0x5A) and np.all(sh[nb:] == -7.0)
+
+
+def test_pi05_reduce_k8_every_element_by_the_oracle():
+    """All 437,500,000 outputs of the k = 8 reduce (fp32 and bf16) against the oracle."""
+    dev = require_gpu()
+    n, k = workloads.PI05_SHARD_N, workloads.PI05_PEERS
+    shards = [workloads.random_wire_shard(n, seed=200 + p, fmt=fq.E4M3, device=dev) for p in range(k)]
+    qs = [a for a, _ in shards]
+    ss = [b for _, b in shards]
+    y = fq.fp8q_dequant_reduce(qs, ss, fq.E4M3)
+    yb = fq.fp8q_dequant_reduce(qs, ss, fq.E4M3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    batch = 1 << 26
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        for a in range(0, n, batch):
+            b = min(n, a + batch)
+            qh = [host(q[a:b]) for q in qs]
+            sh = [host(s[a // 128:(b + 127) // 128]) for s in ss]
+            yh, ybh = host(y[a:b]), host(yb[a:b])
+            parts = _pieces(0, b - a, 4 * _threads(), 128)
+
+            def run(p, bf):
+                i, j = p
+                return oracle.dequant_reduce([v[i:j] for v in qh],
+                                             [v[i // 128:(j + 127) // 128] for v in sh],
+                                             fq.E4M3, out_bf16=bf)
+            want = np.concatenate(list(ex.map(lambda p: run(p, False), parts)))
+            want_b = np.concatenate(list(ex.map(lambda p: run(p, True), parts)))
+            assert_bytes_equal(f32_bits(yh), f32_bits(want), "fp32 [%d, %d)" % (a, b))
+            assert_bf16_parity(ybh, want_b, "bf16 [%d, %d)" % (a, b))
+
+
+def test_moe_layer_mx8_every_row_by_the_oracle():
+    """Every row of the 128-expert gate, up and down tensors against the oracle."""
+    dev = require_gpu()
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        for name, w in workloads.moe_layer(seed=0, device=dev).items():
+            q, e = fq.mx8_quantize(w)
+            torch.cuda.synchronize()
+            K = w.shape[-1]
+            rows = w.numel() // K
+            wb = workloads.bits(w).reshape(rows, K)
+            parts = _pieces(0, rows, 4 * _threads(), 1)
+            outs = list(ex.map(lambda p: oracle.mx8_quantize(wb[p[0]:p[1]]), parts))
+            assert_bytes_equal(host(q).reshape(rows, K), np.concatenate([o[0] for o in outs]),
+                               name + " codes")
+            assert_bytes_equal(host(e), np.concatenate([o[1] for o in outs]), name + " e8m0")

@@ -121,7 +121,7 @@ def test_ragged_sizes_leave_canaries(n):
     assert np.all(ybh[n:] == 77)
 
 
-@pytest.mark.parametrize("nbytes", workloads.SWEEP_BYTES[:-1])
+@pytest.mark.parametrize("nbytes", workloads.SWEEP_BYTES)
 def test_payload_sweep_e5m2_k8(nbytes):
     dev = require_gpu()
     bits = [workloads.bits(workloads.sweep_payload(nbytes, seed=p)) for p in range(8)]

@@ -407,23 +407,16 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
   const uint64_t w0 = wave_index();
 
   __shared__ float wg_scales[kWgTiles * kTileBlocks];
-  const uint32_t wid = uniform(threadIdx.x / kWave);
-  const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
-  // Same trip count for every wave of the workgroup: the barriers are
-  // reached by all of them.
-  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
-       base += stride) {
-    const uint64_t t0 = base + (uint64_t)wid * T;
-    if (t0 < full_tiles)
-      requant_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
-                                             full_tiles, lane);
-    __syncthreads();
-    const uint64_t left = (full_tiles - base) * kTileBlocks;
-    const uint32_t nb = left < (uint64_t)(kWgTiles * kTileBlocks) ? (uint32_t)left
-                                                                 : kWgTiles * kTileBlocks;
-    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) so[base * kTileBlocks + i] = wg_scales[i];
-    if (base + stride < full_tiles) __syncthreads();   // before the next round reuses it
-  }
+  workgroup_rounds<T>(
+      full_tiles,
+      [&](uint64_t t0, uint32_t wid) {
+        requant_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
+                                               full_tiles, lane);
+      },
+      [&](uint64_t base, uint32_t tiles) {
+        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += blockDim.x)
+          so[base * kTileBlocks + i] = wg_scales[i];
+      });
   if (w0 == nw - 1)
     requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
 }

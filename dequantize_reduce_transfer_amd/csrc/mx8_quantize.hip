@@ -146,29 +146,22 @@ __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u
 
   __shared__ uint32_t wg_e8m0[kWgTiles * kTileBytes / 4];
   uint8_t *stage = reinterpret_cast<uint8_t *>(wg_e8m0);
-  const uint32_t wid = uniform(threadIdx.x / kWave);
-  const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
   const bool words = (reinterpret_cast<uintptr_t>(e8m0) & 3u) == 0;
-  // Same trip count for every wave of the workgroup: the barriers are
-  // reached by all of them.
-  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
-       base += stride) {
-    const uint64_t t0 = base + (uint64_t)wid * T;
-    if (t0 < full_tiles)
-      mx_wave_tiles<U, T>(w, q, stage + wid * T * kTileBytes, t0, full_tiles, lane);
-    __syncthreads();
-    const uint64_t left = (full_tiles - base) * kTileBytes;
-    const uint32_t nb = left < (uint64_t)(kWgTiles * kTileBytes) ? (uint32_t)left
-                                                                : kWgTiles * kTileBytes;
-    uint8_t *dst = e8m0 + base * kTileBytes;
-    if (words) {
-      for (uint32_t i = threadIdx.x; i < nb / 4; i += blockDim.x)
-        reinterpret_cast<uint32_t *>(dst)[i] = wg_e8m0[i];
-    } else {
-      for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) dst[i] = stage[i];
-    }
-    if (base + stride < full_tiles) __syncthreads();   // before the next round reuses it
-  }
+  workgroup_rounds<T>(
+      full_tiles,
+      [&](uint64_t t0, uint32_t wid) {
+        mx_wave_tiles<U, T>(w, q, stage + wid * T * kTileBytes, t0, full_tiles, lane);
+      },
+      [&](uint64_t base, uint32_t tiles) {
+        const uint32_t nb = tiles * kTileBytes;
+        uint8_t *dst = e8m0 + base * kTileBytes;
+        if (words) {
+          for (uint32_t i = threadIdx.x; i < nb / 4; i += blockDim.x)
+            reinterpret_cast<uint32_t *>(dst)[i] = wg_e8m0[i];
+        } else {
+          for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) dst[i] = stage[i];
+        }
+      });
   // Tail: whole blocks only (the element count is a multiple of 32, so every
   // quad of chunks is either entirely present or entirely absent).
   if (w0 == nw - 1) {

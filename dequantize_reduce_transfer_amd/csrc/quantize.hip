@@ -152,8 +152,37 @@ __device__ __forceinline__ void quantize_tile(const u32x4 (&v)[U], u32x2 *__rest
   }
 }
 
-// Each wave takes T consecutive tiles; the next tile's loads are issued
-// before the current tile's arithmetic.  The workgroup's 4T tiles stage
+// A wave's T consecutive tiles [t0, t0 + T) (those below full_tiles), the
+// next tile's loads issued before the current tile's arithmetic; tile
+// t0 + j puts its scales at sc_dst + 4U * j.
+template <int FMT, int U, int T>
+__device__ __forceinline__ void quantize_wave_tiles(const u32x4 *__restrict__ x,
+                                                    u32x2 *__restrict__ q, float *sc_dst,
+                                                    uint64_t t0, uint64_t full_tiles,
+                                                    uint32_t lane) {
+  constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
+  u32x4 cur[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = ld(x + t0 * kChunks + u * kWave + lane);
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const uint64_t t = t0 + j;
+    if (t >= full_tiles) break;
+    u32x4 nxt[U];
+    const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u] = ld(x + (t + 1) * kChunks + u * kWave + lane);
+    }
+    quantize_tile<FMT, U>(cur, q, sc_dst + 4 * U * j, t, lane);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+  }
+}
+
+// Each wave takes T consecutive tiles.  The workgroup's 4T tiles stage
 // their 16UT scales in LDS, and one wave writes them to HBM as one
 // contiguous store (whole 128-byte lines).  Storing each tile's 16U bytes
 // from its own wave, as partial lines, measured 2-8% slower at 16 MiB -
@@ -164,49 +193,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__
                                                        float *__restrict__ scales, uint64_t n,
                                                        uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
-  constexpr int kTileBlocks = 4 * U;
-  constexpr int kWgTiles = kWgWaves * T;
+  constexpr uint32_t kTileBlocks = 4 * U;
+  __shared__ float wg_scales[kWgWaves * T * kTileBlocks];
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index();
-
-  __shared__ float wg_scales[kWgTiles * kTileBlocks];
-  const uint32_t wid = uniform(threadIdx.x / kWave);
-  const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
-  // The trip count is the same for every wave of the workgroup, so the
-  // barriers below are reached by all of them.
-  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
-       base += stride) {
-    const uint64_t t0 = base + (uint64_t)wid * T;
-    if (t0 < full_tiles) {
-      u32x4 cur[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) cur[u] = ld(x + t0 * kChunks + u * kWave + lane);
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const uint64_t t = t0 + j;
-        if (t >= full_tiles) break;
-        u32x4 nxt[U];
-        const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-        if (more) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) nxt[u] = ld(x + (t + 1) * kChunks + u * kWave + lane);
-        }
-        quantize_tile<FMT, U>(cur, q, wg_scales + (wid * T + j) * kTileBlocks, t, lane);
-        if (more) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
-      }
-    }
-    __syncthreads();
-    const uint64_t left = (full_tiles - base) * kTileBlocks;
-    const uint32_t nb = left < (uint64_t)(kWgTiles * kTileBlocks) ? (uint32_t)left
-                                                                 : kWgTiles * kTileBlocks;
-    for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) scales[base * kTileBlocks + i] = wg_scales[i];
-    if (base + stride < full_tiles) __syncthreads();   // before the next round reuses the array
-  }
-  if (w0 == nw - 1)
+  workgroup_rounds<T>(
+      full_tiles,
+      [&](uint64_t t0, uint32_t wid) {
+        quantize_wave_tiles<FMT, U, T>(x, q, wg_scales + wid * T * kTileBlocks, t0, full_tiles,
+                                       lane);
+      },
+      [&](uint64_t base, uint32_t tiles) {
+        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += blockDim.x)
+          scales[base * kTileBlocks + i] = wg_scales[i];
+      });
+  if (wave_index() == wave_count() - 1)
     quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
                        scales, n, full_tiles * kChunks * 8);
 }

@@ -18,8 +18,9 @@
  *
  * Conventions shared by every entry point
  *   - Data pointers are DEVICE pointers.  Arrays of pointers (the peers of
- *     fp8q_dequant_reduce / fp8q_sum_f32) are HOST arrays of device pointers,
- *     read before the call returns.
+ *     fp8q_dequant_reduce, fp8q_dequant_reduce_requantize,
+ *     mx8_dequant_reduce and fp8q_sum_f32) are HOST arrays of device
+ *     pointers, read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued on it and the call returns without synchronising.
  *   - The caller owns every buffer.  The library allocates no device memory,

@@ -165,14 +165,15 @@ __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1)
 #ifndef FP8Q_XCD_CHUNK
 #define FP8Q_XCD_CHUNK 64
 #endif
+template <int C = FP8Q_XCD_CHUNK>
 __device__ __forceinline__ uint32_t block_position() {
   const uint32_t b = blockIdx.x, g = gridDim.x;
-  if constexpr (FP8Q_XCD_CHUNK > 0) {
-    constexpr uint32_t kRound = 8u * FP8Q_XCD_CHUNK;
+  if constexpr (C > 0) {
+    constexpr uint32_t kRound = 8u * C;
     if (b >= g / kRound * kRound) return b;
     const uint32_t m = b % kRound;
-    return b - m + (m % 8u) * FP8Q_XCD_CHUNK + m / 8u;
-  } else if constexpr (FP8Q_XCD_CHUNK < 0) {
+    return b - m + (m % 8u) * C + m / 8u;
+  } else if constexpr (C < 0) {
     const uint32_t whole = g / 8u * 8u;
     if (b >= whole) return b;
     return (b % 8u) * (whole / 8u) + b / 8u;
@@ -181,9 +182,11 @@ __device__ __forceinline__ uint32_t block_position() {
   }
 }
 
-// Global wave index and wave count of a 1-D launch of 256-thread workgroups.
+// Global wave index and wave count of a 1-D launch of 256-thread workgroups
+// (the workgroup placed by block_position<C>).
+template <int C = FP8Q_XCD_CHUNK>
 __device__ __forceinline__ uint32_t wave_index() {
-  return uniform(block_position() * (blockDim.x / kWave) + threadIdx.x / kWave);
+  return uniform(block_position<C>() * (blockDim.x / kWave) + threadIdx.x / kWave);
 }
 __device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (blockDim.x / kWave); }
 

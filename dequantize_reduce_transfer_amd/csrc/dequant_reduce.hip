@@ -47,16 +47,22 @@ namespace {
 #ifndef FP8Q_RED_T
 #define FP8Q_RED_T 2         // consecutive tiles per wave (pipelined)
 #endif
-// The dequantize (k == 1) has its own knobs.  On MI355X (437.5M elements,
-// and the MXFP8 layer) U = 2, T = 2 beat U = 1, 2, 4 with T = 1, 2, 4 into
-// fp32 and for the MXFP8 layer into bf16; U = 4, T = 1 was 9% faster for the
-// block-128 dequantize into bf16 but 6% slower for the MXFP8 one, which
-// shares the setting, so the default stays.
+// The block-128 dequantize (k == 1) has its own knobs.  On MI355X (437.5M
+// elements) U = 2, T = 2 beat U = 1, 2, 4 with T = 1, 2, 4 into fp32, while
+// into bf16 U = 4, T = 2 was 11% faster than U = 2, T = 2 (and U = 4, T = 1
+// 6% faster).  The MXFP8 receiver keeps U = 2, T = 2 for one shard (U = 4,
+// T = 1 was 6% slower there).
 #ifndef FP8Q_RED_U1
-#define FP8Q_RED_U1 FP8Q_RED_U4   // tile depth of the dequantize (k == 1)
+#define FP8Q_RED_U1 FP8Q_RED_U4   // dequantize into fp32: tile depth
 #endif
 #ifndef FP8Q_RED_T1
-#define FP8Q_RED_T1 FP8Q_RED_T    // tiles per wave of the dequantize (k == 1)
+#define FP8Q_RED_T1 FP8Q_RED_T    // dequantize into fp32: tiles per wave
+#endif
+#ifndef FP8Q_RED_U1_BF16
+#define FP8Q_RED_U1_BF16 4        // dequantize into bf16: tile depth
+#endif
+#ifndef FP8Q_RED_T1_BF16
+#define FP8Q_RED_T1_BF16 2        // dequantize into bf16: tiles per wave
 #endif
 
 struct PeerPtrs {
@@ -74,15 +80,19 @@ struct PartPtrs {
 // plus 2U scales per peer on the scalar path), and the best mix of tile
 // depth and scale path changes with k; see the vector-scale switch below.
 template <int K>
-constexpr int reduce_u() {
-  return K == 1 ? FP8Q_RED_U1
-                : (K <= 4 ? FP8Q_RED_U4
-                          : (K <= 8 ? FP8Q_RED_U8 : (K <= 13 ? FP8Q_RED_U13 : FP8Q_RED_U16)));
+constexpr int peers_u() {
+  return K <= 4 ? FP8Q_RED_U4
+                : (K <= 8 ? FP8Q_RED_U8 : (K <= 13 ? FP8Q_RED_U13 : FP8Q_RED_U16));
 }
 
-template <int K>
+template <int K, bool BF16 = false>
+constexpr int reduce_u() {
+  return K == 1 ? (BF16 ? FP8Q_RED_U1_BF16 : FP8Q_RED_U1) : peers_u<K>();
+}
+
+template <int K, bool BF16 = false>
 constexpr int reduce_t() {
-  return K == 1 ? FP8Q_RED_T1 : FP8Q_RED_T;
+  return K == 1 ? (BF16 ? FP8Q_RED_T1_BF16 : FP8Q_RED_T1) : FP8Q_RED_T;
 }
 
 // XCD run length (block_position) of the block-128 dequantize: 16 measured
@@ -264,8 +274,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
 
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
-  constexpr int U = reduce_u<K>();
-  constexpr int T = reduce_t<K>();
+  constexpr int U = reduce_u<K, BF16>();
+  constexpr int T = reduce_t<K, BF16>();
   const uint64_t tile = (uint64_t)U * 256;
   const uint64_t full = n / tile;
   hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
@@ -568,13 +578,13 @@ __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__re
 // U = 1 beyond (its scales are always vector byte loads).
 template <int K>
 constexpr int mx_reduce_u() {
-  return K <= 8 ? reduce_u<K>() : 1;
+  return K <= 8 ? peers_u<K>() : 1;
 }
 
 template <int K, bool BF16>
 hipError_t launch_mx_reduce_t(const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = mx_reduce_u<K>();
-  constexpr int T = reduce_t<K>();
+  constexpr int T = FP8Q_RED_T;
   const uint64_t full = n / ((uint64_t)U * 256);
   hipLaunchKernelGGL((mx_reduce_kernel<K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
                      dim3(256), 0, stream, P, y, n, full);

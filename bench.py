@@ -442,57 +442,71 @@ def next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out, reps=10):
 
 def k_sweep(torch, fq, q, s, dev, reps=10):
     """Fused reduce into bf16 for k = 1, 2, 4, 8, 16 peers of 218,750,000
-    elements each: 16 distinct block-aligned slices of the quantized
-    gradient, so no peer is read twice."""
+    elements each, taken from 16 distinct block-aligned slices of the
+    quantized gradient.  Launch i reads slices (i * k + j) mod 16, so the
+    inputs rotate through all 3.5 GB and come from HBM, not from the 256 MB
+    Infinity Cache; the output alternates between two buffers."""
     n = q.numel() // 16
     stride = n // 128 * 128
     qs = [q[p * stride:p * stride + n] for p in range(16)]
     ss = [s[p * stride // 128:p * stride // 128 + fq.num_scales(n)] for p in range(16)]
-    y = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
     out = []
     for k in (1, 2, 4, 8, 16):
-        f = lambda k=k: fq.fp8q_dequant_reduce(qs[:k], ss[:k], fq.E4M3, out_dtype=torch.bfloat16,
-                                               out=y)
-        f()
-        ms = median_ms(torch, [f] * reps)
+        def launch(i, k=k):
+            sel = [(i * k + j) % 16 for j in range(k)]
+            return lambda: fq.fp8q_dequant_reduce([qs[p] for p in sel], [ss[p] for p in sel],
+                                                  fq.E4M3, out_dtype=torch.bfloat16,
+                                                  out=ys[i % 2])
+        launch(0)()
+        ms = median_ms(torch, [launch(i) for i in range(reps)])
         alg = reduce_bytes_per_elem(k, 2) * n
         out.append({"k": k, "elements": n, "us": round(ms * 1e3, 2),
                     "hbm_GBps": round(alg / ms / 1e6, 1),
                     "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)})
-    del y
+    del ys
     return out
 
 
-def stress_reduce(torch, fq, workloads, dev, reps=20):
+def stress_reduce(torch, fq, workloads, dev, reps=21):
     """k = 8 fused reduce into bf16 over the stress payload's shape: 8 peers x
     33,554,432 elements in 8 all-to-all chunks; "share" is one chunk (one
     GPU's part), "full" is all of it.  The reduce's time does not depend on
-    the code values, so the shards are drawn directly as wire codes."""
+    the code values, so the shards are drawn directly as wire codes.  Seven
+    copies of the 344 MB working set (2.4 GB) rotate from launch to launch so
+    that the data comes from HBM, not from the 256 MB Infinity Cache."""
     n, chunks = workloads.STRESS_N, workloads.STRESS_CHUNKS
+    copies = 7
     res = {}
     for fmt, name in ((fq.E4M3, "e4m3"), (fq.E5M2, "e5m2")):
-        shards = [workloads.random_wire_shard(n, seed=300 + p, fmt=fmt, device=dev) for p in range(8)]
-        y = torch.empty(n, dtype=torch.bfloat16, device=dev)
-        c = n // chunks
+        sets = []
+        for c in range(copies):
+            shards = [workloads.random_wire_shard(n, seed=300 + p, fmt=fmt, device=dev)
+                      for p in range(8)]
+            sets.append((shards, torch.empty(n, dtype=torch.bfloat16, device=dev)))
+        cn = n // chunks
 
         def share(i):
-            j = i % chunks
-            qs = [a[j * c:(j + 1) * c] for a, _ in shards]
-            ss = [b[j * c // 128:(j + 1) * c // 128] for _, b in shards]
+            shards, y = sets[i % copies]
+            j = (i // copies) % chunks
+            qs = [a[j * cn:(j + 1) * cn] for a, _ in shards]
+            ss = [b[j * cn // 128:(j + 1) * cn // 128] for _, b in shards]
             return lambda: fq.fp8q_dequant_reduce(qs, ss, fmt, out_dtype=torch.bfloat16,
-                                                  out=y[j * c:(j + 1) * c])
+                                                  out=y[j * cn:(j + 1) * cn])
 
-        full = lambda: fq.fp8q_dequant_reduce([a for a, _ in shards], [b for _, b in shards], fmt,
-                                              out_dtype=torch.bfloat16, out=y)
+        def full(i):
+            shards, y = sets[i % copies]
+            return lambda: fq.fp8q_dequant_reduce([a for a, _ in shards], [b for _, b in shards],
+                                                  fmt, out_dtype=torch.bfloat16, out=y)
         sm = graph_ms(torch, [share(i) for i in range(reps)])
-        fm = graph_ms(torch, [full for _ in range(reps)])
+        fm = graph_ms(torch, [full(i) for i in range(reps)])
         alg = reduce_bytes_per_elem(8, 2)
-        res[name] = {"share_elements": c, "share_us": round(sm * 1e3, 2),
-                     "share_hbm_GBps": round(alg * c / sm / 1e6, 1),
+        res[name] = {"share_elements": cn, "share_us": round(sm * 1e3, 2),
+                     "share_hbm_GBps": round(alg * cn / sm / 1e6, 1),
                      "full_elements": n, "full_us": round(fm * 1e3, 2),
                      "full_hbm_GBps": round(alg * n / fm / 1e6, 1),
                      "full_frac_peak": round(alg * n / fm / 1e6 / HBM_PEAK_GBS, 4)}
-        del shards, y
+        del sets
     return res
 
 

@@ -367,6 +367,15 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
+// Requantize tile shape: as the reduce (U = 1, or T = 3 or 4, measured
+// 1-10% slower on MI355X at k = 2..16).
+#ifndef FP8Q_RQ_U
+#define FP8Q_RQ_U 0              // requantize tile depth; 0: as the reduce
+#endif
+#ifndef FP8Q_RQ_T
+#define FP8Q_RQ_T FP8Q_RED_T     // requantize tiles per wave
+#endif
+
 // One tile: sum, requantize, store the codes, and put the tile's 2U scales
 // at s_dst[0 .. 2U) in the workgroup's LDS staging array.
 template <int FIN, int FOUT, int K, int U, bool VS>
@@ -445,8 +454,8 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
 
 template <int FIN, int FOUT, int K>
 hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
-  constexpr int U = reduce_u<K>();
-  constexpr int T = FP8Q_RED_T;
+  constexpr int U = FP8Q_RQ_U > 0 ? FP8Q_RQ_U : reduce_u<K>();
+  constexpr int T = FP8Q_RQ_T;
   const uint64_t full = n / ((uint64_t)U * 256);
   hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
                      dim3(256), 0, stream, P, static_cast<uint32_t *>(qo), so, n, full);

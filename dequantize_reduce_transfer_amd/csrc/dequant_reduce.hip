@@ -298,10 +298,23 @@ hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t
 // an FP8 all-reduce sends FP8 again: "FP8 Transmission Optimization for VLA
 // Training", "Threshold Changes" bullet).  The fp32 sums acc_i are block-128
 // quantized directly: amax over the block, s = max(fl32(amax / FP8_MAX),
-// 2^-126), q_i = satRNE(fl32(acc_i / s)).  The sums are fp32 (24-bit
-// significands), outside the bf16 domain the quantize kernel's divide-free
-// quotient was proven on, so each element uses the IEEE divide; the VALU
-// budget of this kernel (k reads per element) has room for it.
+// 2^-126), q_i = satRNE(fl32(acc_i / s)).
+//
+// The quotient without a per-element divide.  Per block: sp = s * f and
+// rp = RN(1 / sp) (IEEE divides), with f = 2^64 for blocks whose amax is
+// below 2^-60 (else 1), so that every residual that can decide a code is a
+// normal number.  Per element, with x' = acc * f (exact):
+//   q0 = RN(x' * rp)
+//   e0 = RN(q0 * sp - x')  q1 = RN(q0 - e0 * rp)     (fused multiply-adds)
+//   e1 = RN(q1 * sp - x')  q2 = RN(q1 - e1 * rp)
+// Markstein's correction, applied twice: q1 is within one ulp of x / s and
+// the second step rounds it correctly.  q2 equals the IEEE quotient for
+// every pair of significands in emulated 8- to 16-bit binary arithmetic
+// (exhaustive) and on 3.6e9 random and boundary-adjacent fp32 pairs (both
+// checked on the host).  Where an intermediate could leave the normal
+// range the quotient is below 2^-26, far under half the smallest FP8
+// subnormal, and the sequence keeps the dividend's sign, so the code is the
+// same signed zero.
 //
 // Same mapping as reduce_kernel: lanes 0-31 of a 256-element group hold one
 // block, lanes 32-63 the next; the block amax is 4 DPP steps within each
@@ -310,7 +323,10 @@ hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
 struct F32Scale {
-  float s;
+  float s;        // the stored scale (NaN for a non-finite block)
+  float sp;       // s * f
+  float rp;       // RN(1 / sp)
+  float f;        // 2^64 for blocks with amax below 2^-60, else 1
   bool finite;
 };
 
@@ -320,13 +336,22 @@ __device__ __forceinline__ F32Scale f32_block_scale(uint32_t amax_bits) {
   r.finite = amax_bits < 0x7F800000u;
   float s = __uint_as_float(amax_bits) / fp8_max<FMT>();    // IEEE fp32 divide
   s = fmaxf(s, 0x1p-126f);
+  r.f = amax_bits < 0x21800000u ? 0x1p64f : 1.0f;          // amax < 2^-60
+  r.sp = s * r.f;
+  r.rp = 1.0f / r.sp;                                       // IEEE fp32 divide
   r.s = r.finite ? s : __uint_as_float(0x7FC00000u);
   return r;
 }
 
 template <int FMT>
-__device__ __forceinline__ float f32_quot(float v, float s) {
-  return __builtin_amdgcn_fmed3f(v / s, -fp8_max<FMT>(), fp8_max<FMT>());   // IEEE divide
+__device__ __forceinline__ float f32_quot(float v, const F32Scale &b) {
+  const float xp = v * b.f;
+  const float q0 = xp * b.rp;
+  const float e0 = __builtin_fmaf(q0, b.sp, -xp);
+  const float q1 = __builtin_fmaf(-e0, b.rp, q0);
+  const float e1 = __builtin_fmaf(q1, b.sp, -xp);
+  const float q2 = __builtin_fmaf(-e1, b.rp, q1);
+  return __builtin_amdgcn_fmed3f(q2, -fp8_max<FMT>(), fp8_max<FMT>());
 }
 
 // Elements [start, n) (start is block-aligned): one block per pass, two
@@ -359,7 +384,7 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
     for (int j = 0; j < 2; ++j) {
       const uint64_t i = b0 + 2 * lane + j;
       if (i < n) {
-        const uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(v[j], sc.s), 0.0f, 0.0f, 0.0f);
+        const uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(v[j], sc), 0.0f, 0.0f, 0.0f);
         qo[i] = sc.finite ? (uint8_t)c : (uint8_t)0x7F;
       }
     }
@@ -393,8 +418,8 @@ __device__ __forceinline__ void requant_tile(const PeerPtrs &P, const TileIn<K, 
 #pragma unroll
     for (int j = 1; j < 4; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
     const F32Scale sc = f32_block_scale<FOUT>(max_half32(m));
-    uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(acc[u][0], sc.s), f32_quot<FOUT>(acc[u][1], sc.s),
-                            f32_quot<FOUT>(acc[u][2], sc.s), f32_quot<FOUT>(acc[u][3], sc.s));
+    uint32_t c = cvt4<FOUT>(f32_quot<FOUT>(acc[u][0], sc), f32_quot<FOUT>(acc[u][1], sc),
+                            f32_quot<FOUT>(acc[u][2], sc), f32_quot<FOUT>(acc[u][3], sc));
     if (!sc.finite) c = 0x7F7F7F7Fu;
     st(qo + dw0 + u * kWave + lane, c);
     if ((lane & 31) == 0) s_dst[2 * u + (upper ? 1 : 0)] = sc.s;

@@ -236,3 +236,31 @@ def test_tensorwise_pi05_gradient_full_sampled():
     q_o, s_o = oracle.quantize_tensorwise(xs, fq.E4M3)
     assert_bytes_equal(f32_bits(host(s)), f32_bits(s_o), "scale")
     assert_bytes_equal(host(q[it]), q_o, "sampled codes")
+
+
+@pytest.mark.parametrize("fmt_out", [fq.E4M3, fq.E5M2])
+def test_requantize_quotient_across_every_scale_range(fmt_out):
+    """Sums whose blocks span fp32 from subnormal to 2^100: block scales set
+    to 2^e * (1 + m) for every exponent e in [-149, 100], so amax falls below
+    2^-60 (the rescaled quotient), near the 2^-126 scale floor and far above,
+    with every code present; compared with the oracle byte for byte."""
+    dev = require_gpu()
+    rng = np.random.default_rng(17)
+    exps = np.arange(-149, 101)
+    nb = exps.size * 4
+    n = nb * 128
+    qs, ss = [], []
+    for p in range(2):
+        q = rng.integers(0, 256, n).astype(np.uint8)
+        q[(q & 0x7F) == 0x7F] ^= 0x01                   # no NaN codes (e4m3 input)
+        sig = 1.0 + rng.random(nb)
+        s = np.ldexp(sig, np.repeat(exps, 4)).astype(np.float32)
+        s[s == 0] = np.float32(2.0 ** -149)
+        qs.append(q)
+        ss.append(s)
+    q_g, s_g = fq.fp8q_dequant_reduce_requantize([dev_u8(a, dev) for a in qs],
+                                                 [dev_f32(b, dev) for b in ss], fq.E4M3, fmt_out)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.reduce_requantize(qs, ss, fq.E4M3, fmt_out)
+    assert_bytes_equal(host(q_g), q_o, "codes")
+    assert_bytes_equal(f32_bits(host(s_g)), f32_bits(s_o), "scales")

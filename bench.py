@@ -524,7 +524,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        sys.stderr.write("bench.py measures one GPU: this build has no multi-GPU path "
+        sys.stderr.write("bench.py measures one GPU: the library has no multi-GPU path "
                          "(got --gpus %d). Run with --gpus 1.\n" % args.gpus)
         sys.exit(2)
 

@@ -21,7 +21,8 @@
  *     fp8q_dequant_reduce, fp8q_dequant_reduce_requantize,
  *     mx8_dequant_reduce and fp8q_sum_f32) are HOST arrays of device
  *     pointers, read before the call returns.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *   - `stream` is a hipStream_t (NULL = the default stream) of the current
+ *     HIP device, and every buffer must live on that device.  Work is
  *     enqueued on it and the call returns without synchronising.
  *   - The caller owns every buffer.  The library allocates no device memory,
  *     keeps no pointer after returning and holds no mutable global state.

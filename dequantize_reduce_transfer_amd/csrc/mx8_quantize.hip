@@ -21,10 +21,12 @@
 // block order, so the kernel never needs rows or K.  A block is 64 bytes = a
 // quad of lanes x 16 B; one wave-wide 16-byte load covers 16 blocks (1 KiB
 // contiguous) and the block amax takes 2 DPP steps.  A tile is U loads (16U
-// blocks); lane 4g + c stores the E8M0 byte of block (u = c, g), so one byte
-// store per lane writes the tile's 16U scale bytes contiguously.  Each wave
-// takes T consecutive tiles, issuing the next tile's loads before the
-// current tile's arithmetic; the grid has one wave per T tiles.
+// blocks); lane 4g + c writes the E8M0 byte of block (u = c, g), so one byte
+// write per lane puts the tile's 16U scale bytes in order into the
+// workgroup's LDS staging array, from which they leave in one contiguous
+// store per workgroup.  Each wave takes T consecutive tiles, issuing the
+// next tile's loads before the current tile's arithmetic; the grid has one
+// wave per T tiles, placed XCD-aware.
 #include "fp8q_device.h"
 #include "launch.h"
 

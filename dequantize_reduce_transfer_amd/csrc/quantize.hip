@@ -13,12 +13,14 @@
 // before any arithmetic; each wave takes T consecutive tiles and issues the
 // next tile's loads before the current tile's arithmetic.  The block amax is
 // an integer max over sign-cleared bf16 bits (packed u16 max inside the
-// lane, then 4 DPP steps across the 16 lanes); no LDS is used.  The grid has
-// one wave per T tiles (grid-stride only past the dispatch limit), so the
-// tiles in flight stay inside one window of the buffer; the last wave also
-// handles the ragged tail (< one tile, possibly a partial block).  Loads and
-// stores are non-temporal: every byte is touched once.  The kernel is bound
-// by HBM bandwidth, not by its arithmetic.
+// lane, then 4 DPP steps across the 16 lanes), so it needs no LDS; LDS only
+// stages a workgroup's scales so that they leave in one contiguous store.
+// The grid has one wave per T tiles (grid-stride only past the dispatch
+// limit), placed XCD-aware (block_position), so the tiles in flight stay
+// inside one window of the buffer; the last wave also handles the ragged
+// tail (< one tile, possibly a partial block).  Loads and stores are
+// non-temporal: every byte is touched once.  The kernel is bound by HBM
+// bandwidth, not by its arithmetic.
 //
 // The quotient without a per-element divide.  Per block: sp = s * f and
 // rp = RN(1 / sp) (one IEEE divide each), with f = 2^64 for blocks whose amax

@@ -168,22 +168,26 @@ def _cpu_pieces(smp, fmt, threads):
     return jobs
 
 
-def cpu_baseline(smp, fmt, threads):
+def cpu_baseline(smp, fmt, threads, runs=1):
     """The oracle, as it stands, on the sample; with threads > 1 the same
     calls run on independent block-aligned pieces from a thread pool (the
-    oracle's C calls release the GIL), as an OpenMP loop over blocks would."""
+    oracle's C calls release the GIL), as an OpenMP loop over blocks would.
+    The time is the median of `runs` runs."""
     from concurrent.futures import ThreadPoolExecutor
 
     jobs = _cpu_pieces(smp, fmt, threads)
-    t0 = time.perf_counter()
-    if threads == 1:
-        for j in jobs:
-            j()
-    else:
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            for f in [ex.submit(j) for j in jobs]:
-                f.result()
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        if threads == 1:
+            for j in jobs:
+                j()
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                for f in [ex.submit(j) for j in jobs]:
+                    f.result()
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     k = len(smp["qs"])
     bf16_bytes = (2 * smp["n_q"] + 2 * k * smp["n_r"]
                   + sum(2 * w.size for w in smp["ws"].values()))
@@ -194,8 +198,10 @@ def cpu_baseline(smp, fmt, threads):
         "kind": "oracle",
         "sample": ("first %.4g of each input: quantize %d elements, dequant-reduce k=%d x %d "
                    "elements, mx8 %d experts of each of 3 tensors; %.2f s wall on %d host "
-                   "thread%s" % (smp["frac"], smp["n_q"], k, smp["n_r"], smp["e_mx"], dt, threads,
-                                 "" if threads == 1 else "s, block-aligned pieces")),
+                   "thread%s, median of %d run%s" % (
+                       smp["frac"], smp["n_q"], k, smp["n_r"], smp["e_mx"], dt, threads,
+                       "" if threads == 1 else "s, block-aligned pieces", runs,
+                       "" if runs == 1 else "s")),
     }
 
 
@@ -713,7 +719,7 @@ def main():
         smp["frac"] = args.cpu_frac
         threads = host_threads()
         log("CPU baseline: oracle on %.4g of the workload, %d threads" % (args.cpu_frac, threads))
-        out["cpu_baseline"] = cpu_baseline(smp, fmt, threads)
+        out["cpu_baseline"] = cpu_baseline(smp, fmt, threads, runs=3 if threads > 1 else 1)
         if threads > 1:
             log("CPU baseline: the same sample on one thread")
             side["cpu_baseline_1_thread"] = cpu_baseline(smp, fmt, 1)

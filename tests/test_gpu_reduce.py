@@ -210,3 +210,31 @@ def test_bf16_output_overflow_rounds_like_rne():
     qq[0] = 0x38
     y = host(fq.fp8q_dequant_reduce([dev_u8(qq, dev)] * 2, [dev_f32(big, dev)] * 2, 0))
     assert np.isinf(y[0]) and y[0] > 0
+
+
+@pytest.mark.parametrize("k", [3, 9, 14])
+def test_scales_at_odd_word_offsets(k):
+    """Scale arrays only 4-byte aligned (odd word offsets into a larger
+    buffer), on the scalar-scale (k = 3, 14) and vector-scale (k = 9) paths,
+    for the reduce and the requantize."""
+    dev = require_gpu()
+    n = 128 * 2000 + 33
+    nb = (n + 127) // 128
+    shards = [workloads.random_wire_shard(n, seed=500 + p, fmt=fq.E4M3) for p in range(k)]
+    qh = [a.numpy() for a, _ in shards]
+    sh = [b.numpy() for _, b in shards]
+    qd = [dev_u8(a, dev) for a in qh]
+    sd = []
+    for p, s in enumerate(sh):
+        off = 2 * p + 1                                # an odd number of floats
+        buf = torch.zeros(nb + off + 3, dtype=torch.float32, device=dev)
+        buf[off:off + nb] = torch.from_numpy(s).to(dev)
+        sd.append(buf[off:off + nb])
+        assert sd[-1].data_ptr() % 8 == 4
+    y = fq.fp8q_dequant_reduce(qd, sd, fq.E4M3)
+    q_r, s_r = fq.fp8q_dequant_reduce_requantize(qd, sd, fq.E4M3, fq.E5M2)
+    torch.cuda.synchronize()
+    assert_bytes_equal(f32_bits(host(y)), f32_bits(oracle.dequant_reduce(qh, sh, fq.E4M3)), "reduce")
+    q_o, s_o = oracle.reduce_requantize(qh, sh, fq.E4M3, fq.E5M2)
+    assert_bytes_equal(host(q_r), q_o, "requantize codes")
+    assert_bytes_equal(f32_bits(host(s_r)), f32_bits(s_o), "requantize scales")

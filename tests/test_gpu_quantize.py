@@ -120,3 +120,22 @@ def test_failed_call_writes_nothing():
         fq.fp8q_quantize(x, 7, q_out=q, scales_out=s)
     torch.cuda.synchronize()
     assert torch.all(q == 0x5A) and torch.all(s == 3.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_scale_outputs_at_odd_word_offsets(fmt):
+    """scales_out only 4-byte aligned (odd word offsets): the workgroup's
+    staged scales still land in place, and the words around them stay."""
+    dev = require_gpu()
+    n = 8192 * 37 + 300                          # several workgroup rounds and a tail
+    nb = (n + 127) // 128
+    x = workloads.segmented_gradient(n, seed=12, device=dev, segment=1 << 14)
+    q_o, s_o = oracle.quantize(workloads.bits(x), fmt)
+    for off in (1, 3):
+        buf = torch.full((nb + off + 5,), -2.5, dtype=torch.float32, device=dev)
+        q, s = fq.fp8q_quantize(x, fmt, scales_out=buf[off:off + nb])
+        torch.cuda.synchronize()
+        b = host(buf)
+        assert_bytes_equal(host(q), q_o, "codes")
+        assert_bytes_equal(f32_bits(b[off:off + nb]), f32_bits(s_o), "scales")
+        assert np.all(b[:off] == -2.5) and np.all(b[off + nb:] == -2.5)

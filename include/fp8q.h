@@ -76,7 +76,10 @@ typedef enum {
                                      or a size above FP8Q_MAX_ELEMS            */
     FP8Q_ERR_ALIGN = 3,           /* a pointer breaks the alignment rule        */
     FP8Q_ERR_OVERLAP = 4,         /* an output overlaps an input or an output   */
-    FP8Q_ERR_HIP = 5              /* the HIP runtime reported an error          */
+    FP8Q_ERR_HIP = 5              /* the HIP runtime reported an error when the
+                                     kernels were enqueued (hipGetLastError,
+                                     which also returns, and clears, an error
+                                     left by earlier work in the thread)        */
 } fp8q_status;
 
 /*

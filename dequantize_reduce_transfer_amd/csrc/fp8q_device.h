@@ -135,6 +135,40 @@ __device__ __forceinline__ float fp8_max() {
   return FMT == 0 ? 448.0f : 57344.0f;
 }
 
+// The block scale max(RN(amax / FP8_MAX), 2^-126) without a divide.
+// FP8_MAX = 7 * 2^m (m = 6 for e4m3, 13 for e5m2), so the quotient is
+// RN(amax / 7) scaled by 2^-m, exactly, wherever it is at least 2^-126; below
+// that the clamp gives 2^-126 either way.  RN(amax / 7) is one Markstein step
+// from c = RN(1/7):
+//   q0 = RN(amax * c),  r = amax - 7 q0 (fma, exact),  t = RN(q0 + r * c) (fma).
+// t equals the IEEE quotient amax / 7 for every finite non-negative fp32
+// amax, and the clamped result equals the IEEE-divide scale for both formats
+// (each checked over all 2^31 such inputs).  A non-finite amax yields 2^-126
+// here (the NaN quotient loses to the clamp); callers store NaN for it.
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  constexpr float c = 0x1.24924ap-3f;                       // RN(1/7)
+  const float q0 = amax * c;
+  const float r = __builtin_fmaf(-q0, 7.0f, amax);
+  const float t = __builtin_fmaf(r, c, q0);
+  return fmaxf(t * (FMT == 0 ? 0x1p-6f : 0x1p-13f), 0x1p-126f);
+}
+
+// RN(1 / x) for a normal x whose reciprocal is normal: the hardware
+// reciprocal (within one ulp) refined by one Newton step in fma.  On MI355X it
+// equals the IEEE divide 1 / x for every such x (checked on the device over
+// all of them).
+__device__ __forceinline__ float recip_rn(float x) {
+  const float r0 = __builtin_amdgcn_rcpf(x);
+  const float e = __builtin_fmaf(-x, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
+
+// True on every lane when some lane of the wave has `pred` set.
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
 // fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
 __device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
   __bf16 x = (__bf16)a;

@@ -22,10 +22,11 @@
 // non-temporal: every byte is touched once.  The kernel is bound by HBM
 // bandwidth, not by its arithmetic.
 //
-// The quotient without a per-element divide.  Per block: sp = s * f and
-// rp = RN(1 / sp) (one IEEE divide each), with f = 2^64 for blocks whose amax
-// is below 2^-60 (else 1) so that every residual below stays a normal number.
-// Per element, with x' = x * f (exact):
+// The quotient without a per-element divide.  Per block: s, sp = s * f and
+// rp = RN(1 / sp), with f = 2^64 for blocks whose amax is below 2^-60 (else
+// 1) so that every residual below stays a normal number; s and rp come from
+// divide-free sequences equal to the IEEE divides (scale_from_amax,
+// recip_rn).  Per element, with x' = x * f (exact):
 //   q0 = RN(x' * rp);  e = RN(q0 * sp - x') (fma, exact);  q1 = RN(q0 - e * rp) (fma)
 // This is Markstein's correction; q1 equals RN(x / s) for every bf16 x and
 // fp32 s that can occur here (exhaustively checked on the host over all
@@ -60,12 +61,10 @@ template <int FMT>
 __device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
   BlockScale b;
   b.finite = amax_bits < 0x7F80u;
-  const float amax = __uint_as_float(amax_bits << 16);
-  float s = amax / fp8_max<FMT>();                 // IEEE fp32 divide
-  s = fmaxf(s, 0x1p-126f);
+  const float s = scale_from_amax<FMT>(__uint_as_float(amax_bits << 16));  // = IEEE amax / M
   b.f = amax_bits < 0x2180u ? 0x1p64f : 1.0f;      // amax < 2^-60
   b.sp = s * b.f;
-  b.rp = 1.0f / b.sp;                              // IEEE fp32 divide
+  b.rp = recip_rn(b.sp);                           // = IEEE 1 / sp
   b.s = b.finite ? s : __uint_as_float(0x7FC00000u);
   return b;
 }

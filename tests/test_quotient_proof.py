@@ -49,3 +49,14 @@ def test_two_step_quotient_random_and_boundary_fp32(tmp_path):
     r = subprocess.run([exe, "20000000", "11"], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "mismatches=0" in r.stdout
+
+
+def test_divide_free_block_scale_exhaustive(tmp_path):
+    """The kernels' block scale without a divide (RN(amax / 7) by one
+    Markstein step from RN(1/7), then the power-of-two factor and the
+    2^-126 clamp) equals max(RN(amax / M), 2^-126) for every finite
+    non-negative fp32 amax, for M = 448 and 57344."""
+    exe = _build(tmp_path, "scale_div7_exhaust.c", "scale_div7_exhaust", extra=("-fopenmp",))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "mismatches: 0" in r.stdout

@@ -394,13 +394,15 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
-// Requantize tile shape: as the reduce (U = 1, or T = 3 or 4, measured
-// 1-10% slower on MI355X at k = 2..16).
+// Requantize tile shape: the reduce's tile depth U, and T = 4 tiles per
+// wave.  On MI355X, T = 4 measured 5-10% faster than T = 2 at k = 1..4 and
+// 2-3% at k = 10..12, and the same at k = 8 and 16.  T = 3, 6 and 8, U = 1
+// and scalar input scales were slower; U = 4 matched it at k = 1 and 2 only.
 #ifndef FP8Q_RQ_U
 #define FP8Q_RQ_U 0              // requantize tile depth; 0: as the reduce
 #endif
 #ifndef FP8Q_RQ_T
-#define FP8Q_RQ_T FP8Q_RED_T     // requantize tiles per wave
+#define FP8Q_RQ_T 4              // requantize tiles per wave
 #endif
 
 // One tile: sum, requantize, store the codes, and put the tile's 2U scales

@@ -446,31 +446,41 @@ def next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out, reps=10):
     return res
 
 
-def k_sweep(torch, fq, q, s, dev, reps=10):
-    """Fused reduce into bf16 for k = 1, 2, 4, 8, 16 peers of 218,750,000
-    elements each, taken from 16 distinct block-aligned slices of the
-    quantized gradient.  Launch i reads slices (i * k + j) mod 16, so the
-    inputs rotate through all 3.5 GB and come from HBM, not from the 256 MB
-    Infinity Cache; the output alternates between two buffers."""
+def k_sweep(torch, fq, q, s, dev, reps=10, requantize=False):
+    """Fused reduce into bf16 (or, with requantize, reduce -> e4m3 requantize)
+    for k = 1, 2, 4, 8, 16 peers of 218,750,000 elements each, taken from 16
+    distinct block-aligned slices of the quantized gradient.  Launch i reads
+    slices (i * k + j) mod 16, so the inputs rotate through all 3.5 GB and
+    come from HBM, not from the 256 MB Infinity Cache; the output alternates
+    between two buffers."""
     n = q.numel() // 16
     stride = n // 128 * 128
     qs = [q[p * stride:p * stride + n] for p in range(16)]
     ss = [s[p * stride // 128:p * stride // 128 + fq.num_scales(n)] for p in range(16)]
-    ys = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    if requantize:
+        outs = [(torch.empty(n, dtype=torch.uint8, device=dev),
+                 torch.empty(fq.num_scales(n), dtype=torch.float32, device=dev)) for _ in range(2)]
+        out_bytes = 1 + 4 / 128
+    else:
+        outs = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        out_bytes = 2
     out = []
     for k in (1, 2, 4, 8, 16):
         def launch(i, k=k):
             sel = [(i * k + j) % 16 for j in range(k)]
-            return lambda: fq.fp8q_dequant_reduce([qs[p] for p in sel], [ss[p] for p in sel],
-                                                  fq.E4M3, out_dtype=torch.bfloat16,
-                                                  out=ys[i % 2])
+            qk, sk = [qs[p] for p in sel], [ss[p] for p in sel]
+            if requantize:
+                return lambda: fq.fp8q_dequant_reduce_requantize(
+                    qk, sk, fq.E4M3, fq.E4M3, q_out=outs[i % 2][0], scales_out=outs[i % 2][1])
+            return lambda: fq.fp8q_dequant_reduce(qk, sk, fq.E4M3, out_dtype=torch.bfloat16,
+                                                  out=outs[i % 2])
         launch(0)()
         ms = median_ms(torch, [launch(i) for i in range(reps)])
-        alg = reduce_bytes_per_elem(k, 2) * n
+        alg = reduce_bytes_per_elem(k, out_bytes) * n
         out.append({"k": k, "elements": n, "us": round(ms * 1e3, 2),
                     "hbm_GBps": round(alg / ms / 1e6, 1),
                     "frac_peak": round(alg / ms / 1e6 / HBM_PEAK_GBS, 4)})
-    del ys
+    del outs
     return out
 
 
@@ -668,6 +678,7 @@ def main():
         side.update(next_rows(torch, fq, workloads, dev, x, qs, ss, moe, mx_out))
         log("side figures: peer-count sweep")
         side["reduce_k_sweep_bf16"] = k_sweep(torch, fq, q, s, dev)
+        side["requantize_k_sweep_e4m3"] = k_sweep(torch, fq, q, s, dev, requantize=True)
         log("side figures: tiny gradient (cache-resident)")
         side["tiny_gradient"] = tiny_config(torch, fq, workloads, dev)
         log("side figures: payload sweep (e5m2) and stress reduce (bf16 out)")

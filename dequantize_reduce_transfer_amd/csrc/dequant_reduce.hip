@@ -305,18 +305,15 @@ hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t
 // 1), so that every residual that can decide a code is a normal number; s
 // and rp come from divide-free sequences equal to the IEEE divides
 // (scale_from_amax, recip_rn).  Per element, with x' = acc * f (exact;
-// skipped for a load whose blocks all have f = 1):
-//   q0 = RN(x' * rp)
-//   e0 = RN(q0 * sp - x')  q1 = RN(q0 - e0 * rp)     (fused multiply-adds)
-//   e1 = RN(q1 * sp - x')  q2 = RN(q1 - e1 * rp)
-// Markstein's correction, applied twice: q1 is within one ulp of x / s and
-// the second step rounds it correctly.  q2 equals the IEEE quotient for
-// every pair of significands in emulated 8- to 16-bit binary arithmetic
-// (exhaustive) and on 3.6e9 random and boundary-adjacent fp32 pairs (both
-// checked on the host).  Where an intermediate could leave the normal
-// range the quotient is below 2^-26, far under half the smallest FP8
-// subnormal, and the sequence keeps the dividend's sign, so the code is the
-// same signed zero.
+// skipped for a load whose blocks all have f = 1), one Markstein step:
+//   q0 = RN(x' * rp);  e = RN(q0 * sp - x') (fma);  q1 = RN(q0 - e * rp) (fma)
+// (markstein_quotient).  q1 equals the IEEE quotient for every pair of fp32
+// significands (all 2^46, checked on the device), for every pair in
+// emulated 8- to 16-bit binary arithmetic, and on random and
+// boundary-adjacent fp32 pairs (both checked on the host).  Where an
+// intermediate could leave the normal range the quotient is below 2^-26, far
+// under half the smallest FP8 subnormal, and the sequence keeps the
+// dividend's sign, so the code is the same signed zero.
 //
 // Same mapping as reduce_kernel: lanes 0-31 of a 256-element group hold one
 // block, lanes 32-63 the next; the block amax is 4 DPP steps within each
@@ -348,12 +345,8 @@ __device__ __forceinline__ F32Scale f32_block_scale(uint32_t amax_bits) {
 template <int FMT, bool SCALED = true>
 __device__ __forceinline__ float f32_quot(float v, const F32Scale &b) {
   const float xp = SCALED ? v * b.f : v;
-  const float q0 = xp * b.rp;
-  const float e0 = __builtin_fmaf(q0, b.sp, -xp);
-  const float q1 = __builtin_fmaf(-e0, b.rp, q0);
-  const float e1 = __builtin_fmaf(q1, b.sp, -xp);
-  const float q2 = __builtin_fmaf(-e1, b.rp, q1);
-  return __builtin_amdgcn_fmed3f(q2, -fp8_max<FMT>(), fp8_max<FMT>());
+  return __builtin_amdgcn_fmed3f(markstein_quotient(xp, b.sp, b.rp), -fp8_max<FMT>(),
+                                fp8_max<FMT>());
 }
 
 // Elements [start, n) (start is block-aligned): one block per pass, two

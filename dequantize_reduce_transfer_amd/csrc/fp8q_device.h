@@ -164,6 +164,18 @@ __device__ __forceinline__ float recip_rn(float x) {
   return __builtin_fmaf(e, r0, r0);
 }
 
+// RN(x / s) of an fp32 x without a divide, given rp = RN(1 / s): one
+// Markstein correction step,
+//   q0 = RN(x * rp),  e = RN(q0 * s - x) (fma),  q1 = RN(q0 - e * rp) (fma).
+// q1 equals the IEEE divide x / s for every pair of fp32 significands (all
+// 2^46, checked on the device), hence for all x, s whose intermediates stay
+// normal, since each step scales exactly with powers of two of x and s.
+__device__ __forceinline__ float markstein_quotient(float x, float s, float rp) {
+  const float q0 = x * rp;
+  const float e = __builtin_fmaf(q0, s, -x);
+  return __builtin_fmaf(-e, rp, q0);
+}
+
 // True on every lane when some lane of the wave has `pred` set.
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;

@@ -28,9 +28,10 @@
 // divide-free sequences equal to the IEEE divides (scale_from_amax,
 // recip_rn).  Per element, with x' = x * f (exact):
 //   q0 = RN(x' * rp);  e = RN(q0 * sp - x') (fma, exact);  q1 = RN(q0 - e * rp) (fma)
-// This is Markstein's correction; q1 equals RN(x / s) for every bf16 x and
-// fp32 s that can occur here (exhaustively checked on the host over all
-// significand pairs, including signed zeros).  q1 is then clamped to
+// This is Markstein's correction (markstein_quotient); q1 equals RN(x / s)
+// for every bf16 x and fp32 s that can occur here (exhaustively checked on
+// the host over all significand pairs, including signed zeros, and on the
+// device over all pairs of fp32 significands).  q1 is then clamped to
 // +-FP8_MAX -- which cannot change an RNE result, since |x / s| exceeds
 // FP8_MAX by at most one fp32 rounding -- and converted by the hardware
 // packed FP8 conversion (round to nearest even).
@@ -71,11 +72,8 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
 
 template <int FMT>
 __device__ __forceinline__ float quotient(float x, const BlockScale &b) {
-  const float xp = x * b.f;
-  const float q0 = xp * b.rp;
-  const float e = __builtin_fmaf(q0, b.sp, -xp);
-  const float q1 = __builtin_fmaf(-e, b.rp, q0);
-  return __builtin_amdgcn_fmed3f(q1, -fp8_max<FMT>(), fp8_max<FMT>());
+  return __builtin_amdgcn_fmed3f(markstein_quotient(x * b.f, b.sp, b.rp), -fp8_max<FMT>(),
+                                fp8_max<FMT>());
 }
 
 template <int FMT>

@@ -1,9 +1,9 @@
 /*
- * The fp32-dividend quotient sequence against the IEEE fp32 divide, on
- * random and adversarial pairs (fp32 arithmetic with explicit fmaf; built
- * with -ffp-contract=off):
+ * The kernels' divide-free quotient of an fp32 dividend against the IEEE
+ * fp32 divide, on random and adversarial pairs (fp32 arithmetic with
+ * explicit fmaf; built with -ffp-contract=off):
  *   y = 1/b (IEEE);  q0 = a*y;  e0 = fma(q0, b, -a);  q1 = fma(-e0, y, q0);
- *   e1 = fma(q1, b, -a);  q2 = fma(-e1, y, q1);   claim: q2 == a/b.
+ *   claim: q1 == a/b.
  * Pairs: (1) random significands and exponents with |a/b| in [2^-40, 2^10];
  * (2) adversarial: b random, a = fl(m * b) +- up to 3 ulps for m a random
  * fp32 midpoint (an odd multiple of half an ulp), so a/b sits next to a
@@ -25,9 +25,7 @@ static float seq(float a, float b) {
   volatile float y = 1.0f / b;
   float q0 = a * y;
   volatile float e0 = fmaf(q0, b, -a);
-  float q1 = fmaf(-e0, y, q0);
-  volatile float e1 = fmaf(q1, b, -a);
-  return fmaf(-e1, y, q1);
+  return fmaf(-e0, y, q0);
 }
 
 static long check(float a, float b) {

@@ -30,21 +30,23 @@ def _build(tmp_path, src, name, extra=()):
     return exe
 
 
-def test_two_step_quotient_exhaustive_in_emulated_precisions(tmp_path):
-    """The requantize kernel's fp32-dividend quotient (two Markstein steps
-    from RN(x * RN(1/s))) equals RN(x / s) for every pair of p-bit
-    significands, p = 8 .. 13, in emulated p-bit arithmetic.  (p = 14 .. 16
-    also pass; they take minutes: build with -DPMIN=14 -DPMAX=16.)"""
+def test_quotient_exhaustive_in_emulated_precisions(tmp_path):
+    """The kernels' quotient of a dividend as precise as the divisor (one
+    Markstein step from RN(x * RN(1/s))) equals RN(x / s) for every pair of
+    p-bit significands, p = 8 .. 13, in emulated p-bit arithmetic, and so
+    does a second step.  (p = 14 .. 16 also pass; they take minutes: build
+    with -DPMIN=14 -DPMAX=16.)"""
     exe = _build(tmp_path, "markstein_emulate.c", "markstein_emulate")
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("one-step mismatches=0") == 6
     assert r.stdout.count("two-step mismatches=0") == 6
 
 
-def test_two_step_quotient_random_and_boundary_fp32(tmp_path):
-    """The same sequence in real fp32 (hardware fma) against the IEEE divide
-    on random pairs and on pairs whose quotient sits next to an fp32
-    rounding boundary, plus signed zeros."""
+def test_quotient_random_and_boundary_fp32(tmp_path):
+    """The same one-step sequence in real fp32 (hardware fma) against the
+    IEEE divide on random pairs and on pairs whose quotient sits next to an
+    fp32 rounding boundary, plus signed zeros."""
     exe = _build(tmp_path, "quotient_f32_random.c", "quotient_f32_random")
     r = subprocess.run([exe, "20000000", "11"], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr

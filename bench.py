@@ -49,8 +49,11 @@ QUANT_KERNEL_SRCS = [os.path.join(ROOT, "dequantize_reduce_transfer_amd", "csrc"
                      for f in ("quantize.hip", "fp8q_device.h", "launch.h")]
 
 
+_T0 = time.perf_counter()
+
+
 def log(msg):
-    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.write("[bench %6.1fs] %s\n" % (time.perf_counter() - _T0, msg))
     sys.stderr.flush()
 
 

@@ -387,16 +387,26 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
-// Requantize tile shape: the reduce's tile depth U, and T = 4 tiles per
-// wave.  On MI355X, T = 4 measured 5-10% faster than T = 2 at k = 1..4 and
-// 2-3% at k = 10..12, and the same at k = 8 and 16.  T = 3, 6 and 8, U = 1
-// and scalar input scales were slower; U = 4 matched it at k = 1 and 2 only.
+// Requantize tile shape, by peer count (measured on MI355X).  U = 2 at every
+// k: at k = 9..12 it beats the reduce's U = 1 by 11-18% (3 waves per SIMD
+// instead of 4, but twice the loads in flight per wave).  T = 4 tiles per
+// wave, except at k = 9..12 where T = 2 measured 2-3% faster; T = 4 beat
+// T = 2 by 5-10% at k = 1..4 and tied at k = 8 and 14..16.  T = 3, 6 and 8,
+// U = 1 and scalar input scales were slower.
 #ifndef FP8Q_RQ_U
-#define FP8Q_RQ_U 0              // requantize tile depth; 0: as the reduce
+#define FP8Q_RQ_U 0              // requantize tile depth; 0: by k as below
 #endif
 #ifndef FP8Q_RQ_T
-#define FP8Q_RQ_T 4              // requantize tiles per wave
+#define FP8Q_RQ_T 0              // requantize tiles per wave; 0: by k as below
 #endif
+template <int K>
+constexpr int requant_u() {
+  return FP8Q_RQ_U > 0 ? FP8Q_RQ_U : 2;
+}
+template <int K>
+constexpr int requant_t() {
+  return FP8Q_RQ_T > 0 ? FP8Q_RQ_T : (K >= 9 && K <= 12 ? 2 : 4);
+}
 
 // One tile: sum, requantize, store the codes, and put the tile's 2U scales
 // at s_dst[0 .. 2U) in the workgroup's LDS staging array.
@@ -483,8 +493,8 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
 
 template <int FIN, int FOUT, int K>
 hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
-  constexpr int U = FP8Q_RQ_U > 0 ? FP8Q_RQ_U : reduce_u<K>();
-  constexpr int T = FP8Q_RQ_T;
+  constexpr int U = requant_u<K>();
+  constexpr int T = requant_t<K>();
   const uint64_t full = n / ((uint64_t)U * 256);
   hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
                      dim3(256), 0, stream, P, static_cast<uint32_t *>(qo), so, n, full);

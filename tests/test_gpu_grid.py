@@ -38,7 +38,7 @@ def test_reduce_many_rounds(k):
     assert_bf16_parity(host(y), oracle.dequant_reduce(qh, sh, fq.E4M3, out_bf16=True), "k=%d" % k)
 
 
-@pytest.mark.parametrize("k", [2, 9, 16])
+@pytest.mark.parametrize("k", [2, 9, 12, 13, 16])
 def test_requantize_many_rounds(k):
     dev = require_gpu()
     n = 4_600_050

@@ -99,15 +99,23 @@ def _check(status: int, what: str) -> None:
         raise Fp8qError(status, "%s: %s" % (what, fp8q_status_str(status)))
 
 
-def _run(what: str, tensors, fn, *args) -> None:
+def _run(what: str, tensors, fn, *args, stream=None) -> None:
     """Call a C entry point with every tensor on one GPU, that GPU current
-    (the library launches on the current HIP device)."""
+    (the library launches on the current HIP device).  When the caller names
+    a stream, every tensor is recorded on it, so that torch's caching
+    allocator does not hand a tensor's memory to new work while the kernels
+    enqueued there may still read or write it."""
     dev = tensors[0].device
     for t in tensors[1:]:
         if t.device != dev:
             raise ValueError("%s: all tensors must be on %s, got one on %s" % (what, dev, t.device))
+    if stream is not None and stream.device != dev:
+        raise ValueError("%s: the stream is on %s, the tensors on %s" % (what, stream.device, dev))
     with torch.cuda.device(dev):
         _check(fn(*args), what)
+    if stream is not None:
+        for t in tensors:
+            t.record_stream(stream)
 
 
 def _stream(t: torch.Tensor, stream) -> int:
@@ -163,7 +171,7 @@ def fp8q_quantize(x: torch.Tensor, fmt: int = E4M3, q_out: Optional[torch.Tensor
     if q_out.numel() != n or scales_out.numel() != num_scales(n):
         raise ValueError("q_out must hold n codes and scales_out ceil(n/128) scales")
     _run("fp8q_quantize", [x, q_out, scales_out], lib().fp8q_quantize, x.data_ptr(), n,
-         _fmt(fmt), q_out.data_ptr(), scales_out.data_ptr(), _stream(x, stream))
+         _fmt(fmt), q_out.data_ptr(), scales_out.data_ptr(), _stream(x, stream), stream=stream)
     return q_out, scales_out
 
 
@@ -181,7 +189,7 @@ def fp8q_dequantize(q: torch.Tensor, scales: torch.Tensor, fmt: int = E4M3,
     if out.numel() != n:
         raise ValueError("out must hold n values")
     _run("fp8q_dequantize", [q, scales, out], lib().fp8q_dequantize, q.data_ptr(),
-         scales.data_ptr(), n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(q, stream))
+         scales.data_ptr(), n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(q, stream), stream=stream)
     return out
 
 
@@ -206,7 +214,7 @@ def fp8q_dequant_reduce(qs: Sequence[torch.Tensor], scales: Sequence[torch.Tenso
     if out.numel() != n:
         raise ValueError("out must hold n values")
     _run("fp8q_dequant_reduce", [*qs, *scales, out], lib().fp8q_dequant_reduce, _ptrs(qs),
-         _ptrs(scales), k, n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream))
+         _ptrs(scales), k, n, _fmt(fmt), out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream), stream=stream)
     return out
 
 
@@ -229,7 +237,7 @@ def mx8_quantize(w: torch.Tensor, q_out: Optional[torch.Tensor] = None,
     if q_out.numel() != w.numel() or e8m0_out.numel() != rows * (K // MX_BLOCK):
         raise ValueError("output sizes do not match w")
     _run("mx8_quantize", [w, q_out, e8m0_out], lib().mx8_quantize, w.data_ptr(), rows, K,
-         q_out.data_ptr(), e8m0_out.data_ptr(), _stream(w, stream))
+         q_out.data_ptr(), e8m0_out.data_ptr(), _stream(w, stream), stream=stream)
     return q_out, e8m0_out
 
 
@@ -250,7 +258,7 @@ def fp8q_sum_f32(parts: Sequence[torch.Tensor], out_dtype=torch.float32,
     if out.numel() != n:
         raise ValueError("out must hold n values")
     _run("fp8q_sum_f32", [*parts, out], lib().fp8q_sum_f32, _ptrs(parts), k, n, out.data_ptr(),
-         _out_code(out_dtype), _stream(parts[0], stream))
+         _out_code(out_dtype), _stream(parts[0], stream), stream=stream)
     return out
 
 
@@ -280,7 +288,7 @@ def fp8q_dequant_reduce_requantize(qs: Sequence[torch.Tensor], scales: Sequence[
         raise ValueError("q_out must hold n codes and scales_out ceil(n/128) scales")
     _run("fp8q_dequant_reduce_requantize", [*qs, *scales, q_out, scales_out],
          lib().fp8q_dequant_reduce_requantize, _ptrs(qs), _ptrs(scales), k, n, _fmt(fmt_in),
-         _fmt(fmt_out), q_out.data_ptr(), scales_out.data_ptr(), _stream(qs[0], stream))
+         _fmt(fmt_out), q_out.data_ptr(), scales_out.data_ptr(), _stream(qs[0], stream), stream=stream)
     return q_out, scales_out
 
 
@@ -306,7 +314,7 @@ def mx8_dequant_reduce(qs: Sequence[torch.Tensor], e8m0s: Sequence[torch.Tensor]
     if out.numel() != qs[0].numel():
         raise ValueError("out must hold rows * K values")
     _run("mx8_dequant_reduce", [*qs, *e8m0s, out], lib().mx8_dequant_reduce, _ptrs(qs),
-         _ptrs(e8m0s), k, rows, K, out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream))
+         _ptrs(e8m0s), k, rows, K, out.data_ptr(), _out_code(out_dtype), _stream(qs[0], stream), stream=stream)
     return out
 
 
@@ -327,7 +335,7 @@ def mx8_dequantize(q: torch.Tensor, e8m0: torch.Tensor, out_dtype=torch.float32,
     if out.numel() != q.numel():
         raise ValueError("out must hold rows * K values")
     _run("mx8_dequantize", [q, e8m0, out], lib().mx8_dequantize, q.data_ptr(), e8m0.data_ptr(),
-         rows, K, out.data_ptr(), _out_code(out_dtype), _stream(q, stream))
+         rows, K, out.data_ptr(), _out_code(out_dtype), _stream(q, stream), stream=stream)
     return out
 
 
@@ -345,5 +353,5 @@ def fp8q_quantize_tensorwise(x: torch.Tensor, fmt: int = E4M3, q_out: Optional[t
     if q_out.numel() != n or scale_out.numel() != 1:
         raise ValueError("q_out must hold n codes and scale_out one scale")
     _run("fp8q_quantize_tensorwise", [x, q_out, scale_out], lib().fp8q_quantize_tensorwise,
-         x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(), scale_out.data_ptr(), _stream(x, stream))
+         x.data_ptr(), n, _fmt(fmt), q_out.data_ptr(), scale_out.data_ptr(), _stream(x, stream), stream=stream)
     return q_out, scale_out

@@ -59,3 +59,46 @@ def test_threads_on_separate_streams_match_serial():
     for i in range(len(jobs)):
         for a, b in zip(got[i], want[i]):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i
+
+
+def _chain_on(x, w, k, st):
+    """_chain with every call given the stream explicitly (no stream context)."""
+    q, s = fq.fp8q_quantize(x, fq.E4M3, stream=st)
+    n = x.numel() // k // 128 * 128
+    qs = [q[p * n:(p + 1) * n] for p in range(k)]
+    ss = [s[p * n // 128:(p + 1) * n // 128] for p in range(k)]
+    y = fq.fp8q_dequant_reduce(qs, ss, fq.E4M3, out_dtype=torch.bfloat16, stream=st)
+    rq, rs = fq.fp8q_dequant_reduce_requantize(qs, ss, fq.E4M3, fq.E5M2, stream=st)
+    wq, we = fq.mx8_quantize(w, stream=st)
+    return [q, s, y, rq, rs, wq, we]
+
+
+def test_explicit_stream_argument_matches_current_stream():
+    """Outputs the binding allocates for a call on a caller-named stream stay
+    that call's while the stream runs, even as the current stream allocates
+    and frees memory meanwhile; the results equal the same chain run on the
+    current stream."""
+    dev = require_gpu()
+    x = workloads.segmented_gradient((1 << 22) + 128, seed=60, device=dev, segment=1 << 20)
+    w = workloads.kaiming_uniform((256, 1024), seed=61, device=dev)
+    want = _chain(x, w, 4)
+    want_dq = fq.fp8q_dequantize(want[0], want[1], fq.E4M3)
+    want_mx = fq.mx8_dequantize(want[5], want[6], out_dtype=torch.bfloat16)
+    want_tw = fq.fp8q_quantize_tensorwise(x, fq.E5M2)
+    torch.cuda.synchronize()
+
+    st = torch.cuda.Stream(device=dev)
+    st.wait_stream(torch.cuda.current_stream(dev))
+    got = _chain_on(x, w, 4, st)
+    got_dq = fq.fp8q_dequantize(got[0], got[1], fq.E4M3, stream=st)
+    got_mx = fq.mx8_dequantize(got[5], got[6], out_dtype=torch.bfloat16, stream=st)
+    got_tw = fq.fp8q_quantize_tensorwise(x, fq.E5M2, stream=st)
+    for _ in range(8):                  # allocator churn on the current stream
+        junk = torch.full((1 << 22,), 7, dtype=torch.uint8, device=dev)
+        del junk
+    st.synchronize()
+    torch.cuda.synchronize()
+    pairs = list(zip(got, want)) + [(got_dq, want_dq), (got_mx, want_mx)]
+    pairs += list(zip(got_tw, want_tw))
+    for i, (a, b) in enumerate(pairs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i

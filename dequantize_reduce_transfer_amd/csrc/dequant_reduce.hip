@@ -345,8 +345,7 @@ __device__ __forceinline__ F32Scale f32_block_scale(uint32_t amax_bits) {
 template <int FMT, bool SCALED = true>
 __device__ __forceinline__ float f32_quot(float v, const F32Scale &b) {
   const float xp = SCALED ? v * b.f : v;
-  return __builtin_amdgcn_fmed3f(markstein_quotient(xp, b.sp, b.rp), -fp8_max<FMT>(),
-                                fp8_max<FMT>());
+  return sat_clamp<FMT>(markstein_quotient(xp, b.sp, b.rp));
 }
 
 // Elements [start, n) (start is block-aligned): one block per pass, two

@@ -135,6 +135,16 @@ __device__ __forceinline__ float fp8_max() {
   return FMT == 0 ? 448.0f : 57344.0f;
 }
 
+// The encode step every kernel takes before cvt4: clamp to +-FP8_MAX
+// (v_med3_f32), so that the packed conversion only rounds and the codec's
+// saturation comes from the clamp.  An input beyond the range, +-inf
+// included, becomes the largest finite code of its sign.  Callers never pass
+// NaN (blocks holding a non-finite value take the all-0x7F path instead).
+template <int FMT>
+__device__ __forceinline__ float sat_clamp(float v) {
+  return __builtin_amdgcn_fmed3f(v, -fp8_max<FMT>(), fp8_max<FMT>());
+}
+
 // The block scale max(RN(amax / FP8_MAX), 2^-126) without a divide.
 // FP8_MAX = 7 * 2^m (m = 6 for e4m3, 13 for e5m2), so the quotient is
 // RN(amax / 7) scaled by 2^-m, exactly, wherever it is at least 2^-126; below

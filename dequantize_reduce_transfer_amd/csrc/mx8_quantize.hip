@@ -60,7 +60,7 @@ __device__ __forceinline__ MxScale mx_scale(uint32_t amax_bits) {
 }
 
 __device__ __forceinline__ float mx_q(float x, float mul) {
-  return __builtin_amdgcn_fmed3f(x * mul, -448.0f, 448.0f);
+  return sat_clamp<0>(x * mul);
 }
 
 __device__ __forceinline__ u32x2 mx_quant8(u32x4 v, const MxScale &m) {

@@ -72,8 +72,7 @@ __device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
 
 template <int FMT>
 __device__ __forceinline__ float quotient(float x, const BlockScale &b) {
-  return __builtin_amdgcn_fmed3f(markstein_quotient(x * b.f, b.sp, b.rp), -fp8_max<FMT>(),
-                                fp8_max<FMT>());
+  return sat_clamp<FMT>(markstein_quotient(x * b.f, b.sp, b.rp));
 }
 
 template <int FMT>

@@ -11,8 +11,16 @@
 // NaN (a block holding a non-finite value writes 0x7F codes without
 // converting), and the oracle's NaN code is a reading of its own.
 //
-// Output: one line per format, then "values: N mismatches: M".  Exit status
-// 0 only when every compared pattern agrees.
+// The same program checks the bf16 outputs' rounding: bf16_pack2 (the
+// kernels' fp32 -> bf16 store conversion) on the device against the oracle's
+// f32_to_bf16 (round to nearest even, overflow to inf), again for all 2^32
+// fp32 patterns.  Here NaN inputs can reach the conversion (a NaN code or
+// scale makes a NaN sum); the oracle reads every NaN as 0x7FC0, and NaN
+// patterns are counted apart ("bf16 nan: ... differ").
+//
+// Output: one line per pass, then "values: N mismatches: M" over the
+// non-NaN patterns of all passes.  Exit status 0 only when all of those
+// agree.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -25,6 +33,7 @@
 #include "fp8q_device.h"
 
 extern "C" uint8_t oracle_fp8_encode(double y, int fmt);
+extern "C" uint16_t oracle_f32_to_bf16(float f);
 
 #define CHECK(x)                                                                      \
   do {                                                                                \
@@ -55,17 +64,30 @@ __global__ __launch_bounds__(256) void encode_patterns(uint32_t first, uint32_t 
   }
 }
 
+// Word w of the chunk holds the bf16 of patterns first + 2w (low half) and
+// first + 2w + 1 (high half).  first + 2w + 1 <= 2^32 - 1 for every chunk.
+__global__ __launch_bounds__(256) void bf16_patterns(uint32_t first, uint32_t *out,
+                                                     uint32_t words) {
+  for (uint32_t w = blockIdx.x * blockDim.x + threadIdx.x; w < words;
+       w += gridDim.x * blockDim.x) {
+    const uint32_t b = first + 2u * w;
+    out[w] = fp8q::bf16_pack2(__uint_as_float(b), __uint_as_float(b + 1u));
+  }
+}
+
 bool is_nan_pattern(uint32_t b) { return (b & 0x7F800000u) == 0x7F800000u && (b & 0x007FFFFFu); }
 
 struct Tally {
-  uint64_t compared = 0, mismatches = 0;
-  uint32_t first_bad = 0;
-  uint8_t got = 0, want = 0;
+  uint64_t compared = 0, mismatches = 0;   // non-NaN patterns
+  uint64_t nan_compared = 0, nan_differ = 0;
+  uint32_t first_bad = 0, first_nan_differ = 0;
+  uint32_t got = 0, want = 0, nan_got = 0;
 };
 
-// Host comparison of one chunk, split over threads.
-Tally compare_chunk(const uint8_t *codes, uint32_t first, int fmt, unsigned threads) {
-  const uint32_t n = 4u * kChunkWords;
+// Host comparison of one chunk of n patterns from `first`, split over
+// threads.  fmt 0 / 1: FP8 codes (one byte each, NaN patterns skipped);
+// fmt 2: bf16 (two bytes each, NaN patterns counted apart).
+Tally compare_chunk(const uint8_t *out, uint32_t first, uint32_t n, int fmt, unsigned threads) {
   std::vector<Tally> part(threads);
   std::vector<std::thread> pool;
   for (unsigned t = 0; t < threads; ++t) {
@@ -75,15 +97,32 @@ Tally compare_chunk(const uint8_t *codes, uint32_t first, int fmt, unsigned thre
       Tally &r = part[t];
       for (uint32_t i = lo; i < hi; ++i) {
         const uint32_t b = first + i;
-        if (is_nan_pattern(b)) continue;
         float v;
         memcpy(&v, &b, 4);
-        const uint8_t want = oracle_fp8_encode((double)v, fmt);
+        uint32_t got, want;
+        if (fmt < 2) {
+          if (is_nan_pattern(b)) continue;
+          got = out[i];
+          want = oracle_fp8_encode((double)v, fmt);
+        } else {
+          uint16_t h;
+          memcpy(&h, out + 2 * (size_t)i, 2);
+          got = h;
+          want = oracle_f32_to_bf16(v);
+          if (is_nan_pattern(b)) {
+            ++r.nan_compared;
+            if (got != want && r.nan_differ++ == 0) {
+              r.first_nan_differ = b;
+              r.nan_got = got;
+            }
+            continue;
+          }
+        }
         ++r.compared;
-        if (codes[i] != want) {
+        if (got != want) {
           if (r.mismatches == 0) {
             r.first_bad = b;
-            r.got = codes[i];
+            r.got = got;
             r.want = want;
           }
           ++r.mismatches;
@@ -99,8 +138,14 @@ Tally compare_chunk(const uint8_t *codes, uint32_t first, int fmt, unsigned thre
       sum.got = r.got;
       sum.want = r.want;
     }
+    if (r.nan_differ && !sum.nan_differ) {
+      sum.first_nan_differ = r.first_nan_differ;
+      sum.nan_got = r.nan_got;
+    }
     sum.compared += r.compared;
     sum.mismatches += r.mismatches;
+    sum.nan_compared += r.nan_compared;
+    sum.nan_differ += r.nan_differ;
   }
   return sum;
 }
@@ -112,31 +157,46 @@ int main() {
   threads = std::max(1u, std::min(threads, 16u));
   uint32_t *d_out = nullptr;
   CHECK(hipMalloc(&d_out, (size_t)kChunkWords * 4));
-  std::vector<uint8_t> codes((size_t)kChunkWords * 4);
+  std::vector<uint8_t> out((size_t)kChunkWords * 4);
   uint64_t total_compared = 0, total_bad = 0;
-  for (int fmt = 0; fmt < 2; ++fmt) {
-    uint64_t compared = 0, bad = 0;
-    for (uint64_t first = 0; first < (1ull << 32); first += 4ull * kChunkWords) {
-      if (fmt == 0)
+  const char *names[3] = {"e4m3", "e5m2", "bf16"};
+  for (int pass = 0; pass < 3; ++pass) {
+    // patterns per chunk: 4 per word for the FP8 passes, 2 for bf16
+    const uint64_t per_chunk = (pass < 2 ? 4ull : 2ull) * kChunkWords;
+    Tally all;
+    for (uint64_t first = 0; first < (1ull << 32); first += per_chunk) {
+      if (pass == 0)
         hipLaunchKernelGGL(encode_patterns<0>, dim3(4096), dim3(256), 0, 0, (uint32_t)first,
                            d_out, kChunkWords);
-      else
+      else if (pass == 1)
         hipLaunchKernelGGL(encode_patterns<1>, dim3(4096), dim3(256), 0, 0, (uint32_t)first,
                            d_out, kChunkWords);
+      else
+        hipLaunchKernelGGL(bf16_patterns, dim3(4096), dim3(256), 0, 0, (uint32_t)first, d_out,
+                           kChunkWords);
       CHECK(hipGetLastError());
-      CHECK(hipMemcpy(codes.data(), d_out, codes.size(), hipMemcpyDeviceToHost));
-      const Tally t = compare_chunk(codes.data(), (uint32_t)first, fmt, threads);
-      if (t.mismatches && !bad)
+      CHECK(hipMemcpy(out.data(), d_out, out.size(), hipMemcpyDeviceToHost));
+      const Tally t = compare_chunk(out.data(), (uint32_t)first, (uint32_t)per_chunk, pass,
+                                    threads);
+      if (t.mismatches && !all.mismatches)
         printf("  first mismatch: pattern 0x%08X got 0x%02X want 0x%02X\n", t.first_bad, t.got,
                t.want);
-      compared += t.compared;
-      bad += t.mismatches;
+      if (t.nan_differ && !all.nan_differ)
+        printf("  first NaN that differs: pattern 0x%08X got 0x%04X\n", t.first_nan_differ,
+               t.nan_got);
+      all.compared += t.compared;
+      all.mismatches += t.mismatches;
+      all.nan_compared += t.nan_compared;
+      all.nan_differ += t.nan_differ;
     }
-    printf("%s: compared %llu fp32 patterns (all but NaN), mismatches %llu\n",
-           fmt == 0 ? "e4m3" : "e5m2", (unsigned long long)compared, (unsigned long long)bad);
+    printf("%s: compared %llu fp32 patterns (all but NaN), mismatches %llu\n", names[pass],
+           (unsigned long long)all.compared, (unsigned long long)all.mismatches);
+    if (pass == 2)
+      printf("bf16 nan: %llu NaN patterns, %llu differ from 0x7FC0\n",
+             (unsigned long long)all.nan_compared, (unsigned long long)all.nan_differ);
     fflush(stdout);
-    total_compared += compared;
-    total_bad += bad;
+    total_compared += all.compared;
+    total_bad += all.mismatches;
   }
   CHECK(hipFree(d_out));
   printf("values: %llu mismatches: %llu\n", (unsigned long long)total_compared,

@@ -49,17 +49,21 @@ CVT_BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "cv
 
 def test_encode_step_equals_oracle_for_every_fp32():
     """The kernels' FP8 encode step -- clamp to +-FP8_MAX (sat_clamp), then
-    the gfx950 packed conversion (cvt4) -- run on the device for all 2^32
-    fp32 patterns in e4m3 and in e5m2, each code compared on the host with
-    the oracle's integer-exact satRNE.  NaN patterns (2 * (2^23 - 1) per
-    format) are left out: no kernel converts a NaN.  About 10-60 s, mostly
-    the oracle on the host's threads."""
+    the gfx950 packed conversion (cvt4) -- and their fp32 -> bf16 output
+    conversion (bf16_pack2), run on the device for all 2^32 fp32 patterns,
+    each result compared on the host with the oracle (integer-exact satRNE
+    in e4m3 and e5m2; round-to-nearest-even bf16).  NaN patterns
+    (2 * (2^23 - 1)) are left out of the FP8 passes, since no kernel converts
+    a NaN to FP8, and counted apart in the bf16 pass.  About 15 s, mostly the
+    oracle on the host's threads."""
     require_gpu()
     if not os.path.exists(CVT_BIN):
         pytest.skip("the device check is built by __graft_entry__.build()")
     r = subprocess.run([CVT_BIN], capture_output=True, text=True, timeout=280)
     assert r.returncode == 0, r.stdout + r.stderr
-    per_format = (1 << 32) - 2 * ((1 << 23) - 1)
-    assert "e4m3: compared %d fp32 patterns" % per_format in r.stdout, r.stdout
-    assert "e5m2: compared %d fp32 patterns" % per_format in r.stdout, r.stdout
-    assert "values: %d mismatches: 0" % (2 * per_format) in r.stdout, r.stdout
+    nans = 2 * ((1 << 23) - 1)
+    per_pass = (1 << 32) - nans
+    for name in ("e4m3", "e5m2", "bf16"):
+        assert "%s: compared %d fp32 patterns" % (name, per_pass) in r.stdout, r.stdout
+    assert "values: %d mismatches: 0" % (3 * per_pass) in r.stdout, r.stdout
+    assert "bf16 nan: %d NaN patterns" % nans in r.stdout, r.stdout

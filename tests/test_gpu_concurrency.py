@@ -102,3 +102,35 @@ def test_explicit_stream_argument_matches_current_stream():
     pairs += list(zip(got_tw, want_tw))
     for i, (a, b) in enumerate(pairs):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), i
+
+
+def test_released_outputs_are_not_reused_while_the_named_stream_runs():
+    """Codes and scales the binding allocates for a call on a named stream
+    are released by the caller while a later call queued on that stream has
+    yet to read them; memory of the same size allocated and overwritten on
+    the current stream meanwhile must not be theirs.  A few milliseconds of
+    work on the named stream sit between the call that writes them and the
+    call that reads them, so the current stream's writes land in between."""
+    dev = require_gpu()
+    n = (1 << 22) + 128 * 3
+    x = workloads.segmented_gradient(n, seed=70, device=dev, segment=1 << 20)
+    busy = workloads.sweep_payload(1 << 28, seed=71, device=dev)          # 2^27 bf16
+    q0, s0 = fq.fp8q_quantize(x, fq.E4M3)
+    want = fq.fp8q_dequantize(q0, s0, fq.E4M3)
+    torch.cuda.synchronize()
+
+    st = torch.cuda.Stream(device=dev)
+    st.wait_stream(torch.cuda.current_stream(dev))
+    bq = torch.empty(busy.numel(), dtype=torch.uint8, device=dev)
+    bs = torch.empty(fq.num_scales(busy.numel()), dtype=torch.float32, device=dev)
+    q, s = fq.fp8q_quantize(x, fq.E4M3, stream=st)
+    for _ in range(40):                 # a few ms of work on st between the two calls
+        fq.fp8q_quantize(busy, fq.E4M3, q_out=bq, scales_out=bs, stream=st)
+    got = fq.fp8q_dequantize(q, s, fq.E4M3, stream=st)
+    del q, s                            # released before st has read them
+    junk_q = torch.full((n,), 0x7E, dtype=torch.uint8, device=dev)
+    junk_s = torch.full((fq.num_scales(n),), 1.0e30, dtype=torch.float32, device=dev)
+    st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+    del junk_q, junk_s, bq, bs, busy

@@ -464,19 +464,19 @@ __device__ __forceinline__ void requant_wave_tiles(const PeerPtrs &P, uint32_t *
 // T consecutive tiles per wave.  The workgroup's 4T tiles stage their 8UT
 // scales in LDS, and they leave in one contiguous store rather than as 8UT
 // four-byte stores from different waves (measured 2.7% faster for k = 8).
-template <int FIN, int FOUT, int K, int U, int T>
-__global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
-                                                      float *__restrict__ so, uint64_t n,
-                                                      uint64_t full_tiles) {
+template <int FIN, int FOUT, int K, int U, int T, int W, int C>
+__global__ __launch_bounds__(64 * W) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
+                                                         float *__restrict__ so, uint64_t n,
+                                                         uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
   constexpr uint32_t kTileBlocks = 2 * U;
-  constexpr uint32_t kWgTiles = 4 * T;             // 4 waves per workgroup
+  constexpr uint32_t kWgTiles = W * T;             // W waves per workgroup
   const uint32_t lane = lane_id();
   const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index();
+  const uint64_t w0 = wave_index<C>();
 
   __shared__ float wg_scales[kWgTiles * kTileBlocks];
-  workgroup_rounds<T>(
+  workgroup_rounds<T, W, C>(
       full_tiles,
       [&](uint64_t t0, uint32_t wid) {
         requant_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
@@ -490,13 +490,40 @@ __global__ __launch_bounds__(256) void requant_kernel(PeerPtrs P, uint32_t *__re
     requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
 }
 
-template <int FIN, int FOUT, int K>
-hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
+// Workgroup shape.  4 waves per workgroup (XCD runs of FP8Q_XCD_CHUNK),
+// except for 13 or more peers on at least FP8Q_RQ_WIDE_N elements: there
+// the kernel holds 178-216 VGPRs, 2 waves per SIMD, and a 4-wave workgroup's
+// barrier before the scale flush stalls a large share of the CU; one-wave
+// workgroups (XCD runs of 256, the same bytes per run) measured 1-3% faster
+// at k = 16 for 16 - 256 MiB payloads on MI355X and 8% faster on
+// 218.75M-element shards, but 2% slower at 4 MiB.  For fewer peers the two
+// shapes were within +-2%.
+#ifndef FP8Q_RQ_WIDE_N
+#define FP8Q_RQ_WIDE_N (1ull << 23)
+#endif
+#ifndef FP8Q_RQ_WIDE_K
+#define FP8Q_RQ_WIDE_K 13
+#endif
+
+template <int FIN, int FOUT, int K, int W, int C>
+void launch_requant_shape(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
   constexpr int U = requant_u<K>();
   constexpr int T = requant_t<K>();
   const uint64_t full = n / ((uint64_t)U * 256);
-  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
-                     dim3(256), 0, stream, P, static_cast<uint32_t *>(qo), so, n, full);
+  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T, W, C>),
+                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P,
+                     static_cast<uint32_t *>(qo), so, n, full);
+}
+
+template <int FIN, int FOUT, int K>
+hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
+  if constexpr (K >= FP8Q_RQ_WIDE_K) {
+    if (n >= FP8Q_RQ_WIDE_N) {
+      launch_requant_shape<FIN, FOUT, K, 1, 256>(P, n, qo, so, stream);
+      return hipGetLastError();
+    }
+  }
+  launch_requant_shape<FIN, FOUT, K, 4, FP8Q_XCD_CHUNK>(P, n, qo, so, stream);
   return hipGetLastError();
 }
 

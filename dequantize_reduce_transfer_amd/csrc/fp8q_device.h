@@ -248,20 +248,20 @@ __device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (blockDim.
 
 // Workgroup rounds for kernels that stage a per-tile output (block scales,
 // E8M0 bytes) in LDS and write a workgroup's worth of it as one contiguous
-// store.  The 4-wave workgroup at position p takes the 4T tiles from
-// base = p * 4T, then base += grid * 4T while tiles remain; its wave w takes
-// [base + wT, base + wT + T).  Per round: wave_tiles(t0, w) for each wave
-// with tiles left, a barrier, flush(base, tiles in this round) by the whole
-// workgroup, and, when another round follows, a second barrier before the
-// staging array is reused.  Every wave of a workgroup runs the same number
-// of rounds, so each barrier is reached by all of them.
-template <int T, typename WaveTiles, typename Flush>
+// store.  The W-wave workgroup at position p (block_position<C>) takes the
+// WT tiles from base = p * WT, then base += grid * WT while tiles remain; its
+// wave w takes [base + wT, base + wT + T).  Per round: wave_tiles(t0, w) for
+// each wave with tiles left, a barrier, flush(base, tiles in this round) by
+// the whole workgroup, and, when another round follows, a second barrier
+// before the staging array is reused.  Every wave of a workgroup runs the
+// same number of rounds, so each barrier is reached by all of them.
+template <int T, int W = 4, int C = FP8Q_XCD_CHUNK, typename WaveTiles, typename Flush>
 __device__ __forceinline__ void workgroup_rounds(uint64_t full_tiles, WaveTiles &&wave_tiles,
                                                  Flush &&flush) {
-  constexpr uint32_t kWgTiles = 4 * T;
+  constexpr uint32_t kWgTiles = W * T;
   const uint32_t wid = uniform(threadIdx.x / kWave);
   const uint64_t stride = (uint64_t)gridDim.x * kWgTiles;
-  for (uint64_t base = (uint64_t)block_position() * kWgTiles; base < full_tiles;
+  for (uint64_t base = (uint64_t)block_position<C>() * kWgTiles; base < full_tiles;
        base += stride) {
     const uint64_t t0 = base + (uint64_t)wid * T;
     if (t0 < full_tiles) wave_tiles(t0, wid);

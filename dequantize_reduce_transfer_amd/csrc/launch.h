@@ -16,19 +16,21 @@ namespace fp8q {
 
 constexpr int kMaxPeers = 16;
 
-// Grid size: one 4-wave workgroup per 4 tiles, so that the tiles in flight
-// at any moment form one window of the buffer (measured faster on MI355X
-// than a persistent grid, whose waves drift apart across the whole buffer;
-// the workgroup -> position map inside the window is XCD-aware, see
-// block_position in fp8q_device.h).  The cap keeps grid * 256 work-items inside the dispatch packet's
-// 32-bit range; beyond it the kernels' grid-stride loops take the rest.
+// Grid size: one workgroup of waves_per_wg waves per waves_per_wg units of
+// wave work (the argument counts those units: tiles, or groups of T tiles),
+// so that the tiles in flight at any moment form one window of the buffer
+// (measured faster on MI355X than a persistent grid, whose waves drift apart
+// across the whole buffer; the workgroup -> position map inside the window
+// is XCD-aware, see block_position in fp8q_device.h).  The cap keeps
+// grid * 256 work-items inside the dispatch packet's 32-bit range; beyond it
+// the kernels' grid-stride loops take the rest.
 #ifndef FP8Q_MAX_WORKGROUPS
 #define FP8Q_MAX_WORKGROUPS (1ull << 22)
 #endif
 constexpr uint64_t kMaxWorkgroups = FP8Q_MAX_WORKGROUPS;
 
-inline uint32_t grid_for_tiles(uint64_t tiles) {
-  uint64_t wgs = (tiles + 3) / 4;
+inline uint32_t grid_for_tiles(uint64_t tiles, uint32_t waves_per_wg = 4) {
+  uint64_t wgs = (tiles + waves_per_wg - 1) / waves_per_wg;
   if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
   if (wgs < 1) wgs = 1;
   return (uint32_t)wgs;

@@ -123,7 +123,22 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
   }
 }
 
-constexpr int kWgWaves = 4;                      // waves per 256-thread workgroup
+// Workgroup shape by size.  Below FP8Q_QUANT_WIDE_N elements a workgroup is
+// 4 waves and each XCD run is FP8Q_XCD_CHUNK (64) workgroups; from there up
+// it is one wave, with XCD runs of FP8Q_QUANT_WIDE_XCD (256) workgroups, so
+// an XCD run still covers 1 MiB of bf16.  One-wave workgroups never wait at
+// the barrier before the scale flush for a slower wave.  On MI355X (e4m3,
+// variants alternated in one run) they measured 83.9-84.1% of 8 TB/s on the
+// 3.5e9-element gradient against 81.3-81.8% for 4 waves, 83.3-83.5% against
+// 82.4-82.6% at 512 MiB and 81.2-81.4% against 80.6-80.7% at 256 MiB, but
+// 68.6-69.5% against 70.2-70.4% at 64 MiB, where 4x more workgroups cost
+// more to launch than the barrier does.
+#ifndef FP8Q_QUANT_WIDE_N
+#define FP8Q_QUANT_WIDE_N (1ull << 27)
+#endif
+#ifndef FP8Q_QUANT_WIDE_XCD
+#define FP8Q_QUANT_WIDE_XCD 256
+#endif
 
 // One tile: quantize the U loaded chunks, store the codes, and put the
 // tile's 4U scales at sc_dst[0 .. 4U) in the workgroup's LDS staging array.
@@ -180,21 +195,21 @@ __device__ __forceinline__ void quantize_wave_tiles(const u32x4 *__restrict__ x,
   }
 }
 
-// Each wave takes T consecutive tiles.  The workgroup's 4T tiles stage
-// their 16UT scales in LDS, and one wave writes them to HBM as one
-// contiguous store (whole 128-byte lines).  Storing each tile's 16U bytes
-// from its own wave, as partial lines, measured 2-8% slower at 16 MiB -
-// 1 GiB payloads.
-template <int FMT, int U, int T>
-__global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__ x,
-                                                       u32x2 *__restrict__ q,
-                                                       float *__restrict__ scales, uint64_t n,
-                                                       uint64_t full_tiles) {
+// Each wave takes T consecutive tiles.  The workgroup's WT tiles stage
+// their 4UWT scales in LDS, and they leave in one contiguous store by the
+// whole workgroup.  Storing each tile's 16U bytes from its own wave, as
+// partial lines, measured 2-8% slower at 16 MiB - 1 GiB payloads (with
+// 4-wave workgroups).  W waves per workgroup, XCD runs of C workgroups.
+template <int FMT, int U, int T, int W, int C>
+__global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restrict__ x,
+                                                          u32x2 *__restrict__ q,
+                                                          float *__restrict__ scales, uint64_t n,
+                                                          uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
   constexpr uint32_t kTileBlocks = 4 * U;
-  __shared__ float wg_scales[kWgWaves * T * kTileBlocks];
+  __shared__ float wg_scales[W * T * kTileBlocks];
   const uint32_t lane = lane_id();
-  workgroup_rounds<T>(
+  workgroup_rounds<T, W, C>(
       full_tiles,
       [&](uint64_t t0, uint32_t wid) {
         quantize_wave_tiles<FMT, U, T>(x, q, wg_scales + wid * T * kTileBlocks, t0, full_tiles,
@@ -204,20 +219,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const u32x4 *__restrict__
         for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += blockDim.x)
           scales[base * kTileBlocks + i] = wg_scales[i];
       });
-  if (wave_index() == wave_count() - 1)
+  if (wave_index<C>() == wave_count() - 1)
     quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
                        scales, n, full_tiles * kChunks * 8);
 }
 
-template <int FMT>
-hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
+template <int FMT, int W, int C>
+void launch_shape(const void *x, uint64_t n, void *q, float *scales, uint64_t full,
+                  hipStream_t stream) {
   constexpr int U = kQuantU;
   constexpr int T = kQuantT;
-  const uint64_t tile_elems = (uint64_t)U * kWave * 8;
-  const uint64_t full = n / tile_elems;
-  hipLaunchKernelGGL((quantize_kernel<FMT, U, T>), dim3(grid_for_tiles((full + T - 1) / T)),
-                     dim3(256), 0, stream,
+  hipLaunchKernelGGL((quantize_kernel<FMT, U, T, W, C>),
+                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream,
                      static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, full);
+}
+
+template <int FMT>
+hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
+  const uint64_t tile_elems = (uint64_t)kQuantU * kWave * 8;
+  const uint64_t full = n / tile_elems;
+  if (n >= FP8Q_QUANT_WIDE_N)
+    launch_shape<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream);
+  else
+    launch_shape<FMT, 4, FP8Q_XCD_CHUNK>(x, n, q, scales, full, stream);
   return hipGetLastError();
 }
 

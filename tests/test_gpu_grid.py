@@ -65,3 +65,21 @@ def test_mx8_many_rounds():
     torch.cuda.synchronize()
     assert_bf16_parity(host(y).ravel(), oracle.mx8_dequantize(q_o, e_o, out_bf16=True).ravel(),
                        "mx dequantize")
+
+
+@pytest.mark.parametrize("k", [13, 16])
+def test_requantize_one_wave_workgroups(k):
+    """From 13 peers and 2^23 elements up the requantize runs one-wave
+    workgroups in XCD runs of 256: this size holds two whole rounds of that
+    map at k = 16, a remainder, and a ragged tail of 261 elements."""
+    dev = require_gpu()
+    n = (1 << 23) + 256 * 77 + 5
+    shards = [workloads.random_wire_shard(n, seed=110 + p, fmt=fq.E4M3) for p in range(k)]
+    qh = [a.numpy() for a, _ in shards]
+    sh = [b.numpy() for _, b in shards]
+    q, s = fq.fp8q_dequant_reduce_requantize([dev_u8(a, dev) for a in qh],
+                                             [dev_f32(b, dev) for b in sh], fq.E4M3, fq.E4M3)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.reduce_requantize(qh, sh, fq.E4M3, fq.E4M3)
+    assert_bytes_equal(host(q), q_o, "codes k=%d" % k)
+    assert_bytes_equal(f32_bits(host(s)), f32_bits(s_o), "scales k=%d" % k)

@@ -131,8 +131,8 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 // variants alternated in one run) they measured 83.9-84.1% of 8 TB/s on the
 // 3.5e9-element gradient against 81.3-81.8% for 4 waves, 83.3-83.5% against
 // 82.4-82.6% at 512 MiB and 81.2-81.4% against 80.6-80.7% at 256 MiB, but
-// 68.6-69.5% against 70.2-70.4% at 64 MiB, where 4x more workgroups cost
-// more to launch than the barrier does.
+// 68.6-69.5% against 70.2-70.4% at 64 MiB (there the 4x larger grid seems to
+// cost more than the barrier waits it saves).
 #ifndef FP8Q_QUANT_WIDE_N
 #define FP8Q_QUANT_WIDE_N (1ull << 27)
 #endif

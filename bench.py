@@ -149,7 +149,9 @@ def _piece(total, parts, multiple):
 
 def _cpu_pieces(smp, fmt, threads):
     """The sample's oracle calls, cut at block boundaries into about
-    4 * `threads` independent pieces (one piece each when threads == 1)."""
+    4 * `threads` independent pieces (one piece each when threads == 1).
+    Each job is (what, call): `what` names the output the call's result
+    belongs to, so the pieces can be put back together in order."""
     import oracle
 
     parts = 1 if threads == 1 else 4 * threads
@@ -157,17 +159,17 @@ def _cpu_pieces(smp, fmt, threads):
     xq = smp["x"]
     step = _piece(xq.size, parts, 128)
     for a in range(0, xq.size, step):
-        jobs.append(lambda a=a, m=step: oracle.quantize(xq[a:a + m], fmt))
+        jobs.append(("quantize", lambda a=a, m=step: oracle.quantize(xq[a:a + m], fmt)))
     n_r = smp["n_r"]
     step = _piece(n_r, parts, 128)
     for a in range(0, n_r, step):
-        jobs.append(lambda a=a, m=step: oracle.dequant_reduce(
-            [q[a:a + m] for q in smp["qs"]], [s[a // 128:(a + m) // 128] for s in smp["ss"]], fmt))
-    for w in smp["ws"].values():
+        jobs.append(("dequant_reduce", lambda a=a, m=step: oracle.dequant_reduce(
+            [q[a:a + m] for q in smp["qs"]], [s[a // 128:(a + m) // 128] for s in smp["ss"]], fmt)))
+    for name, w in smp["ws"].items():
         rows = w.shape[0]
         step = _piece(rows, parts, 1)
         for a in range(0, rows, step):
-            jobs.append(lambda w=w, a=a, m=step: oracle.mx8_quantize(w[a:a + m]))
+            jobs.append(("mx8_" + name, lambda w=w, a=a, m=step: oracle.mx8_quantize(w[a:a + m])))
     return jobs
 
 
@@ -175,26 +177,31 @@ def cpu_baseline(smp, fmt, threads, runs=1):
     """The oracle, as it stands, on the sample; with threads > 1 the same
     calls run on independent block-aligned pieces from a thread pool (the
     oracle's C calls release the GIL), as an OpenMP loop over blocks would.
-    The time is the median of `runs` runs."""
+    The time is the median of `runs` runs.  Returns the record and the
+    oracle's outputs of the first run, in order, keyed by output."""
     from concurrent.futures import ThreadPoolExecutor
 
     jobs = _cpu_pieces(smp, fmt, threads)
     times = []
-    for _ in range(runs):
+    outputs = None
+    for r in range(runs):
         t0 = time.perf_counter()
         if threads == 1:
-            for j in jobs:
-                j()
+            res = [j() for _, j in jobs]
         else:
             with ThreadPoolExecutor(max_workers=threads) as ex:
-                for f in [ex.submit(j) for j in jobs]:
-                    f.result()
+                res = [f.result() for f in [ex.submit(j) for _, j in jobs]]
         times.append(time.perf_counter() - t0)
+        if r == 0:
+            outputs = {}
+            for (what, _), o in zip(jobs, res):
+                outputs.setdefault(what, []).append(o)
+        del res
     dt = sorted(times)[len(times) // 2]
     k = len(smp["qs"])
     bf16_bytes = (2 * smp["n_q"] + 2 * k * smp["n_r"]
                   + sum(2 * w.size for w in smp["ws"].values()))
-    return {
+    rec = {
         "value": round(bf16_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
@@ -206,15 +213,168 @@ def cpu_baseline(smp, fmt, threads, runs=1):
                        "" if threads == 1 else "s, block-aligned pieces", runs,
                        "" if runs == 1 else "s")),
     }
+    return rec, outputs
+
+
+# The GPU machine gives each GPU a share of 16 host CPUs (its worker pools are to
+# be sized to that share, whatever the machine's own count is), so the
+# oracle's thread pool is capped there; the record states the machine's
+# count, the process's CPU set and the model next to the threads used.
+HOST_THREAD_CAP = 16
+
+
+def host_cpus():
+    """The host's CPU count, the process's CPU set and the CPU model."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
 
 
 def host_threads():
-    """Host threads for the CPU baseline: the process's CPU set, at most 16."""
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    """Host threads for the CPU baseline: the process's CPU set, at most
+    HOST_THREAD_CAP (the machine's CPU share for one GPU)."""
+    return max(1, min(HOST_THREAD_CAP, host_cpus()["affinity_cpus"]))
+
+
+def _sample_idx(nunits, count, seed, always=()):
+    """Sampled unit indices: the first and last 64, `count` random ones and
+    `always`."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    idx = np.concatenate([np.arange(min(64, nunits)), np.arange(max(0, nunits - 64), nunits),
+                          rng.integers(0, nunits, count), np.asarray(always, dtype=np.int64)])
+    return np.unique(idx[(idx >= 0) & (idx < nunits)])
+
+
+def _host(torch, t):
+    import numpy as np
+
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def step_parity(torch, fmt, smp, outputs, x, q, s, qs, ss, y, moe, mx_out):
+    """The step's own GPU outputs against the oracle.
+
+    1. Every output the CPU baseline's sample covers (the first part of the
+       quantized gradient, of the reduce's output, and of each MoE tensor),
+       against the oracle outputs the baseline's first run produced.
+    2. Sampled units across the whole of each output: 8192 random 128-blocks
+       of the quantized gradient (plus the first and last 64 and the blocks
+       that straddle its 25M-element segments), 16384 reduced elements (plus
+       the last 300, the shard's 96-element last block among them) and 512
+       rows of each MoE tensor.  Each sampled unit depends only on its own
+       inputs, so the oracle runs on just those.
+    Returns a summary; raises AssertionError on the first mismatch."""
+    import numpy as np
+
+    import oracle
+    from dequantize_reduce_transfer_amd import workloads
+
+    def same(got, want, what):
+        got = np.ascontiguousarray(got).ravel()
+        want = np.ascontiguousarray(want).ravel()
+        if got.shape != want.shape or not np.array_equal(got, want):
+            bad = np.nonzero(got != want)[0] if got.shape == want.shape else [-1]
+            raise AssertionError("%s: %d mismatches vs the oracle (first at %s)"
+                                 % (what, len(bad), list(bad[:3])))
+
+    def f32(a):
+        return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+    n_q, n_r = smp["n_q"], smp["n_r"]
+    q_o = np.concatenate([o[0] for o in outputs["quantize"]])
+    s_o = np.concatenate([o[1] for o in outputs["quantize"]])
+    same(_host(torch, q[:n_q]), q_o, "quantize codes (sample)")
+    same(f32(_host(torch, s[:n_q // 128])), f32(s_o), "quantize scales (sample)")
+    same(f32(_host(torch, y[:n_r])), f32(np.concatenate(outputs["dequant_reduce"])),
+         "dequant-reduce fp32 (sample)")
+    mx_rows = 0
+    for name in moe:
+        q_m = np.concatenate([o[0] for o in outputs["mx8_" + name]])
+        e_m = np.concatenate([o[1] for o in outputs["mx8_" + name]])
+        rows, K = q_m.shape
+        same(_host(torch, mx_out[name][0].view(-1, K)[:rows]), q_m, "mx8 %s codes (sample)" % name)
+        same(_host(torch, mx_out[name][1][:rows]), e_m, "mx8 %s e8m0 (sample)" % name)
+        mx_rows += rows
+    covered = {"quantize_elements": int(n_q), "reduce_elements": int(n_r), "mx8_rows": mx_rows}
+
+    dev = q.device
+    nb = x.numel() // 128
+    seg = workloads.PI05_SEGMENT
+    edges = [(j * seg) // 128 for j in range(1, x.numel() // seg)]
+    idx = _sample_idx(nb, 8192, seed=1, always=edges)
+    it = torch.from_numpy(idx).to(dev)
+    qb, sb = oracle.quantize(_host(torch, x[:nb * 128].view(-1, 128)[it]).ravel(), fmt)
+    same(_host(torch, q[:nb * 128].view(-1, 128)[it]), qb, "quantize codes (sampled blocks)")
+    same(f32(_host(torch, s[it])), f32(sb), "quantize scales (sampled blocks)")
+
+    n = y.numel()
+    eidx = _sample_idx(n, 16384, seed=2, always=np.arange(n - 300, n))
+    et = torch.from_numpy(eidx).to(dev)
+    bt = torch.from_numpy(eidx // 128).to(dev)
+    m = eidx.size
+    q_in, s_in = [], []
+    for qp, sp in zip(qs, ss):
+        qq = np.zeros((m, 128), np.uint8)          # each sample is element 0 of its own block
+        qq[:, 0] = _host(torch, qp[et])
+        q_in.append(qq.ravel())
+        s_in.append(_host(torch, sp[bt]))
+    same(f32(_host(torch, y[et])), f32(oracle.dequant_reduce(q_in, s_in, fmt)[::128]),
+         "dequant-reduce fp32 (sampled elements)")
+
+    for j, (name, w) in enumerate(moe.items()):
+        K = w.shape[-1]
+        rows = w.numel() // K
+        ridx = _sample_idx(rows, 512, seed=3 + j)
+        rt = torch.from_numpy(ridx).to(dev)
+        qm, em = oracle.mx8_quantize(_host(torch, w.view(rows, K)[rt]))
+        same(_host(torch, mx_out[name][0].view(rows, K)[rt]), qm, "mx8 %s codes (sampled rows)" % name)
+        same(_host(torch, mx_out[name][1][rt]), em, "mx8 %s e8m0 (sampled rows)" % name)
+    covered.update({"sampled_quantize_blocks": int(idx.size), "sampled_reduce_elements": int(m),
+                    "sampled_mx8_rows_per_tensor": 512})
+    return covered
+
+
+GATE_FRAC = 0.70                 # of the HBM peak, for every op at >= 64 MiB payloads
+
+
+def gates(ops, side):
+    """Pass / fail of every gated point: each op whose per-peer bf16
+    payload is at least 64 MiB must reach GATE_FRAC of the HBM peak."""
+    pts = []
+
+    def add(name, frac):
+        if frac is not None:
+            pts.append({"point": name, "frac_peak": round(frac, 4), "pass": frac >= GATE_FRAC})
+
+    add("quantize_e4m3 3.5e9 elements", ops["quantize_e4m3"]["frac_peak"])
+    add("dequant_reduce_k8_f32 437.5M elements", ops["dequant_reduce_k8_f32"]["frac_peak"])
+    add("mx8_layer 603,979,776 elements", ops["mx8_layer"]["frac_peak"])
+    for row in side.get("payload_sweep_e5m2", []):
+        if row["payload_bytes"] >= 64 << 20:
+            add("payload_sweep quantize_e5m2 %d B" % row["payload_bytes"],
+                row["quantize_hbm_GBps"] / HBM_PEAK_GBS)
+            add("payload_sweep reduce_k8_f32 %d B" % row["payload_bytes"],
+                row["reduce_k8_hbm_GBps"] / HBM_PEAK_GBS)
+    for fmt_name, rec in side.get("stress_reduce_k8_bf16", {}).items():
+        add("stress reduce_k8_bf16 full %s" % fmt_name, rec["full_frac_peak"])
+    return {"threshold_frac_peak": GATE_FRAC, "points": pts,
+            "all_pass": all(p["pass"] for p in pts)}
 
 
 def device_info(torch, dev):
@@ -728,20 +888,40 @@ def main():
         "env": device_info(torch, dev),
     }
 
+    out["gates"] = gates(ops, side)
+
+    parity_error = None
+    out["parity_checked"] = False
     if not args.no_cpu_baseline:
         smp = _cpu_sample(x, peers, moe, args.cpu_frac)
         smp["frac"] = args.cpu_frac
         threads = host_threads()
         log("CPU baseline: oracle on %.4g of the workload, %d threads" % (args.cpu_frac, threads))
-        out["cpu_baseline"] = cpu_baseline(smp, fmt, threads, runs=3 if threads > 1 else 1)
+        rec, outputs = cpu_baseline(smp, fmt, threads, runs=3 if threads > 1 else 1)
+        rec.update(host_cpus())
+        rec["thread_cap"] = HOST_THREAD_CAP
+        rec["thread_cap_reason"] = ("the GPU box's host-CPU share for one GPU; the pool "
+                                    "uses min(cap, affinity_cpus) threads")
+        out["cpu_baseline"] = rec
+        log("parity: the step's outputs against the oracle")
+        try:
+            out["parity"] = step_parity(torch, fmt, smp, outputs, x, q, s, qs, ss, y, moe, mx_out)
+            out["parity_checked"] = True
+        except AssertionError as e:
+            parity_error = str(e)
+            out["parity"] = {"mismatch": parity_error}
+        del outputs
         if threads > 1:
             log("CPU baseline: the same sample on one thread")
-            side["cpu_baseline_1_thread"] = cpu_baseline(smp, fmt, 1)
+            side["cpu_baseline_1_thread"] = cpu_baseline(smp, fmt, 1)[0]
         del smp
     else:
         out["cpu_baseline"] = None
 
     print(json.dumps(out), flush=True)
+    if parity_error is not None:
+        log("PARITY FAILURE: " + parity_error)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -247,3 +247,95 @@ def test_tensorwise_validation():
     assert f(P(x.addr), n, 0, P(q.addr), P(s.addr + 2), None) == ERR_ALIGN
     assert f(P(x.addr), n, 0, P(q.addr), P(x.addr + 1000), None) == ERR_OVERLAP
     assert f(P(x.addr), n, 0, P(q.addr), P(q.addr + 996), None) == ERR_OVERLAP
+
+
+# ---------------------------------------------------------------------------
+# Accepted calls.  The host-check build of the library (csrc/api.hip compiled
+# host-only, with tests/native/abi_stub_launchers.cpp in place of the
+# kernels) records each launch instead of enqueueing it, so a valid call can
+# run on a machine without a GPU: it must reach its launcher exactly once,
+# with the caller's n and k, and every rejected call above must reach none.
+# tests/test_abi_sanitized.py runs this whole file against that build under
+# AddressSanitizer and UndefinedBehaviorSanitizer.
+
+def _stub():
+    L = fq.lib()
+    if not hasattr(L, "fp8q_stub_calls"):
+        pytest.skip("needs the host-check build of the library (FP8Q_LIB)")
+    L.fp8q_stub_calls.restype = ctypes.c_long
+    L.fp8q_stub_last.restype = ctypes.c_char_p
+    L.fp8q_stub_last_n.restype = ctypes.c_ulonglong
+    L.fp8q_stub_last_k.restype = ctypes.c_int
+    return L
+
+
+def _expect_launch(L, status, name, n, k=1):
+    before = L.fp8q_stub_calls()
+    assert status() == OK
+    assert L.fp8q_stub_calls() == before + 1
+    assert L.fp8q_stub_last().decode() == name
+    assert L.fp8q_stub_last_n() == n and L.fp8q_stub_last_k() == k
+
+
+def _expect_no_launch(L, status, want):
+    before = L.fp8q_stub_calls()
+    assert status() == want
+    assert L.fp8q_stub_calls() == before
+
+
+def test_accepted_calls_reach_their_launcher_once():
+    L = _stub()
+    n = 1000
+    x, q, s = Buf(2 * n), Buf(n), Buf(4 * 8)
+    _expect_launch(L, lambda: L.fp8q_quantize(P(x.addr), n, 1, P(q.addr), P(s.addr), None),
+                   "quantize", n)
+    _expect_launch(L, lambda: L.fp8q_quantize_tensorwise(P(x.addr), n, 0, P(q.addr), P(s.addr),
+                                                         None), "quantize_tensorwise", n)
+    y = Buf(4 * n)
+    _expect_launch(L, lambda: L.fp8q_dequantize(P(q.addr), P(s.addr), n, 0, P(y.addr), 1, None),
+                   "dequantize", n)
+    for k in (1, 2, 16):
+        qs = [Buf(n) for _ in range(k)]
+        ss = [Buf(4 * 8) for _ in range(k)]
+        qa, sa = PP(*[b.addr for b in qs]), PP(*[b.addr for b in ss])
+        _expect_launch(L, lambda: L.fp8q_dequant_reduce(qa, sa, k, n, 1, P(y.addr), 0, None),
+                       "dequantize" if k == 1 else "dequant_reduce", n, k)
+        qo, so = Buf(n), Buf(4 * 8)
+        _expect_launch(L, lambda: L.fp8q_dequant_reduce_requantize(
+            qa, sa, k, n, 0, 1, P(qo.addr), P(so.addr), None), "reduce_requantize", n, k)
+        parts = [Buf(4 * n) for _ in range(k)]
+        pa = PP(*[b.addr for b in parts])
+        _expect_launch(L, lambda: L.fp8q_sum_f32(pa, k, n, P(y.addr), 1, None), "sum_f32", n, k)
+    rows, K = 7, 96
+    w, qm, e = Buf(2 * rows * K), Buf(rows * K), Buf(rows * K // 32)
+    _expect_launch(L, lambda: L.mx8_quantize(P(w.addr), rows, K, P(qm.addr), P(e.addr + 1), None),
+                   "mx8_quantize", rows * K)
+    ym = Buf(4 * rows * K)
+    _expect_launch(L, lambda: L.mx8_dequantize(P(qm.addr), P(e.addr + 3), rows, K, P(ym.addr), 0,
+                                               None), "mx8_dequantize", rows * K)
+    qa, ea = PP(qm.addr, qm.addr), PP(e.addr, e.addr + 1)
+    _expect_launch(L, lambda: L.mx8_dequant_reduce(qa, ea, 2, rows, K, P(ym.addr), 1, None),
+                   "mx8_dequant_reduce", rows * K, 2)
+
+
+def test_rejected_and_empty_calls_reach_no_launcher():
+    L = _stub()
+    n = 1000
+    x, q, s, y = Buf(2 * n), Buf(n), Buf(4 * 8), Buf(4 * n)
+    _expect_no_launch(L, lambda: L.fp8q_quantize(None, 0, 0, None, None, None), OK)
+    _expect_no_launch(L, lambda: L.fp8q_quantize(P(x.addr), n, 0, P(x.addr + 16), P(s.addr), None),
+                      ERR_OVERLAP)
+    _expect_no_launch(L, lambda: L.fp8q_quantize(P(x.addr + 2), n, 0, P(q.addr), P(s.addr), None),
+                      ERR_ALIGN)
+    _expect_no_launch(L, lambda: L.fp8q_dequantize(P(q.addr), P(s.addr), n, 0, None, 0, None),
+                      ERR_NULL)
+    qa, sa = PP(q.addr, q.addr), PP(s.addr, s.addr)
+    _expect_no_launch(L, lambda: L.fp8q_dequant_reduce(qa, sa, 2, n, 0, P(y.addr), 9, None),
+                      ERR_ARG)
+    _expect_no_launch(L, lambda: L.fp8q_dequant_reduce_requantize(
+        qa, sa, 2, n, 0, 0, P(q.addr), P(s.addr), None), ERR_OVERLAP)
+    _expect_no_launch(L, lambda: L.mx8_quantize(P(x.addr), 10, 48, P(q.addr), P(s.addr), None),
+                      ERR_ARG)
+    _expect_no_launch(L, lambda: L.mx8_dequant_reduce(qa, sa, 17, 10, 64, P(y.addr), 0, None),
+                      ERR_ARG)
+    _expect_no_launch(L, lambda: L.fp8q_sum_f32(PP(y.addr), 1, n, P(y.addr), 0, None), ERR_OVERLAP)

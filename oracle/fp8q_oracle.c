@@ -27,7 +27,9 @@
  *   the E8M0 scale type and the MX scale-selection rule.
  *
  * Where the pages leave a step open the plainest reading is taken; each such
- * reading is marked READING below.
+ * reading is marked READING below.  One function, the tensorwise quantize,
+ * follows a recipe the pages name without printing its arithmetic: its
+ * parity against that recipe is unpinned (marked PARITY UNPINNED below).
  *
  * Precision.  The method fixes its own arithmetic: an fp32 scale per block,
  * an fp32 quotient that is then rounded to FP8, and fp32 accumulation.  So
@@ -247,6 +249,10 @@ void oracle_quantize(const uint16_t *x, size_t n, int fmt, uint8_t *q, float *sc
 /* section on TorchAO's Float8Linear with the tensorwise recipe) computes    */
 /* amax, scale and cast per tensor.  READING: the same scale rule and floor  */
 /* as the block path, with the block being the whole tensor.                 */
+/* PARITY UNPINNED against that recipe: the page names it but prints none of */
+/* its arithmetic (its scale formula, rounding or floor), and no library     */
+/* implementing it is available here, so this function is pinned only to    */
+/* the block rule (one block spanning the tensor equals block quantize).     */
 /* ------------------------------------------------------------------------ */
 
 void oracle_quantize_tensorwise(const uint16_t *x, size_t n, int fmt, uint8_t *q, float *scale)

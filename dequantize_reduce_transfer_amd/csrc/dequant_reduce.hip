@@ -251,8 +251,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restric
                                                      uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index<reduce_xcd_chunk<K>()>();
+  const uint64_t nw = wave_count<4>();
+  const uint64_t w0 = wave_index<4, reduce_xcd_chunk<K>()>();
 
   constexpr bool VS = kRedVecScales<K>;
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
@@ -472,8 +472,8 @@ __global__ __launch_bounds__(64 * W) void requant_kernel(PeerPtrs P, uint32_t *_
   constexpr uint32_t kTileBlocks = 2 * U;
   constexpr uint32_t kWgTiles = W * T;             // W waves per workgroup
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index<C>();
+  const uint64_t nw = wave_count<W>();
+  const uint64_t w0 = wave_index<W, C>();
 
   __shared__ float wg_scales[kWgTiles * kTileBlocks];
   workgroup_rounds<T, W, C>(
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(64 * W) void requant_kernel(PeerPtrs P, uint32_t *_
                                                full_tiles, lane);
       },
       [&](uint64_t base, uint32_t tiles) {
-        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += blockDim.x)
+        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
           so[base * kTileBlocks + i] = wg_scales[i];
       });
   if (w0 == nw - 1)
@@ -620,8 +620,8 @@ __global__ __launch_bounds__(256) void mx_reduce_kernel(MxPeerPtrs P, void *__re
                                                         uint64_t n, uint64_t full_tiles) {
   constexpr uint64_t kTile = (uint64_t)U * 256;
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index();
+  const uint64_t nw = wave_count<4>();
+  const uint64_t w0 = wave_index<4>();
 
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
     uint32_t cw[K][U], cc[K][U];
@@ -686,9 +686,10 @@ hipError_t dispatch_mx_k(int k, const MxPeerPtrs &P, uint64_t n, void *y, hipStr
 template <bool BF16>
 __global__ __launch_bounds__(256) void sum_kernel(PartPtrs P, int k, void *__restrict__ y,
                                                   uint64_t n) {
+  constexpr uint64_t kThreads = 256;               // the launch's workgroup size
   const uint64_t n4 = n / 4;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
     float4 a = reinterpret_cast<const float4 *>(P.p[0])[i];
     for (int p = 1; p < k; ++p) {
       const float4 b = reinterpret_cast<const float4 *>(P.p[p])[i];

@@ -186,6 +186,11 @@ __device__ __forceinline__ float markstein_quotient(float x, float s, float rp) 
   return __builtin_fmaf(-e, rp, q0);
 }
 
+// s_waitcnt immediate that waits for every vector memory operation of the
+// wave (vmcnt 0, the other counters at their no-wait maxima), in the gfx9
+// encoding: vmcnt in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // True on every lane when some lane of the wave has `pred` set.
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
@@ -238,13 +243,21 @@ __device__ __forceinline__ uint32_t block_position() {
   }
 }
 
-// Global wave index and wave count of a 1-D launch of 256-thread workgroups
-// (the workgroup placed by block_position<C>).
-template <int C = FP8Q_XCD_CHUNK>
+// Global wave index and wave count of a 1-D launch of W-wave workgroups (the
+// workgroup placed by block_position<C>).  W is the workgroup size every
+// launcher here passes for its kernel, a compile-time constant, and no device
+// code reads blockDim: the workgroup size is a 16-bit field of the implicit
+// kernel arguments, which gfx950 reads with a vector load (there is no 16-bit
+// scalar load), and since vector loads and stores share one in-order
+// counter, waiting for that load also waits for every store the wave still
+// has in flight.  On a loaded chip that held each wave of the block quantize
+// for about 3 us after its last store, and with it the wave's slot.
+template <int W, int C = FP8Q_XCD_CHUNK>
 __device__ __forceinline__ uint32_t wave_index() {
-  return uniform(block_position<C>() * (blockDim.x / kWave) + threadIdx.x / kWave);
+  return uniform(block_position<C>() * (uint32_t)W + threadIdx.x / kWave);
 }
-__device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (blockDim.x / kWave); }
+template <int W>
+__device__ __forceinline__ uint32_t wave_count() { return gridDim.x * (uint32_t)W; }
 
 // Workgroup rounds for kernels that stage a per-tile output (block scales,
 // E8M0 bytes) in LDS and write a workgroup's worth of it as one contiguous

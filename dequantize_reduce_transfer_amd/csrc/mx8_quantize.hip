@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u
   constexpr uint32_t kWgTiles = kWgWaves * T;
   const uint32_t lane = lane_id();
   const uint32_t c = lane & 3;
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index();
+  const uint64_t nw = wave_count<kWgWaves>();
+  const uint64_t w0 = wave_index<kWgWaves>();
 
   __shared__ uint32_t wg_e8m0[kWgTiles * kTileBytes / 4];
   uint8_t *stage = reinterpret_cast<uint8_t *>(wg_e8m0);
@@ -158,10 +158,10 @@ __global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u
         const uint32_t nb = tiles * kTileBytes;
         uint8_t *dst = e8m0 + base * kTileBytes;
         if (words) {
-          for (uint32_t i = threadIdx.x; i < nb / 4; i += blockDim.x)
+          for (uint32_t i = threadIdx.x; i < nb / 4; i += 64 * kWgWaves)
             reinterpret_cast<uint32_t *>(dst)[i] = wg_e8m0[i];
         } else {
-          for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) dst[i] = stage[i];
+          for (uint32_t i = threadIdx.x; i < nb; i += 64 * kWgWaves) dst[i] = stage[i];
         }
       });
   // Tail: whole blocks only (the element count is a multiple of 32, so every

@@ -140,6 +140,32 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #define FP8Q_QUANT_WIDE_XCD 256
 #endif
 
+// One-wave workgroups wait for their code stores to be acknowledged before
+// their scales leave (s_waitcnt vmcnt(0) at the top of each round's flush),
+// which keeps each wave, and its slot, until its stores have landed, so
+// fewer waves stream at once.  On MI355X (alternated in one run) the
+// 3.5e9-element quantize took 1583-1589 us with the wait against 1601-1605
+// us without it (1 GiB: 243-244 against 246-247 us; 256 MiB: 62.8-63.0
+// against 63.4-63.6 us).  Waiting only at the end of the wave, after the
+// scales, recovered none of it, and the 4-wave shape is the same either way
+// (64 MiB: 18.1-18.2 us), so it does not wait.
+#ifndef FP8Q_QUANT_FLUSH_WAIT_W1
+#define FP8Q_QUANT_FLUSH_WAIT_W1 1
+#endif
+#ifndef FP8Q_QUANT_FLUSH_WAIT_W4
+#define FP8Q_QUANT_FLUSH_WAIT_W4 0
+#endif
+
+// LDS each 4-wave workgroup reserves beyond its scale staging, so that at
+// most 7 of them share a CU (160 KiB of LDS per CU: 7 x 21 KiB fits, 8 do
+// not), 28 waves instead of 32.  At a 64 MiB payload (two rounds of resident
+// waves) this measured 17.99-18.09 us against 18.10-18.32 us uncapped
+// (alternated in one run on MI355X); a cap of 6 was no faster than none, and
+// 16 and 256 MiB payloads were unchanged.
+#ifndef FP8Q_QUANT_LDS_PAD_W4
+#define FP8Q_QUANT_LDS_PAD_W4 21504
+#endif
+
 // One tile: quantize the U loaded chunks, store the codes, and put the
 // tile's 4U scales at sc_dst[0 .. 4U) in the workgroup's LDS staging array.
 template <int FMT, int U>
@@ -207,7 +233,7 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
                                                           uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
   constexpr uint32_t kTileBlocks = 4 * U;
-  __shared__ float wg_scales[W * T * kTileBlocks];
+  __shared__ float wg_scales[W * T * kTileBlocks + (W == 4 ? FP8Q_QUANT_LDS_PAD_W4 / 4 : 0)];
   const uint32_t lane = lane_id();
   workgroup_rounds<T, W, C>(
       full_tiles,
@@ -216,10 +242,12 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
                                        lane);
       },
       [&](uint64_t base, uint32_t tiles) {
-        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += blockDim.x)
+        if constexpr (W == 1 ? FP8Q_QUANT_FLUSH_WAIT_W1 != 0 : FP8Q_QUANT_FLUSH_WAIT_W4 != 0)
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
           scales[base * kTileBlocks + i] = wg_scales[i];
       });
-  if (wave_index<C>() == wave_count() - 1)
+  if (wave_index<W, C>() == wave_count<W>() - 1)
     quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
                        scales, n, full_tiles * kChunks * 8);
 }
@@ -271,18 +299,23 @@ __global__ __launch_bounds__(64) void tw_zero_kernel(uint32_t *slot) {
 #endif
 constexpr int kAmaxU = FP8Q_AMAX_U;  // 16-byte loads in flight per thread
 
-__global__ __launch_bounds__(256) void tw_amax_kernel(const u32x4 *__restrict__ x, uint64_t n,
-                                                      uint32_t *__restrict__ slot) {
-  __shared__ uint32_t part[4];
+// Launched with 256-thread workgroups (kAmaxThreads); the size is a constant
+// here rather than blockDim (see wave_index in fp8q_device.h).
+constexpr uint32_t kAmaxThreads = 256;
+
+__global__ __launch_bounds__(kAmaxThreads) void tw_amax_kernel(const u32x4 *__restrict__ x,
+                                                               uint64_t n,
+                                                               uint32_t *__restrict__ slot) {
+  __shared__ uint32_t part[kAmaxThreads / kWave];
   const uint64_t nch = n / 8;
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x * kAmaxU;
+  const uint64_t stride = (uint64_t)gridDim.x * kAmaxThreads * kAmaxU;
   uint32_t m = 0;
-  for (uint64_t c0 = (uint64_t)blockIdx.x * blockDim.x * kAmaxU + threadIdx.x; c0 < nch;
+  for (uint64_t c0 = (uint64_t)blockIdx.x * kAmaxThreads * kAmaxU + threadIdx.x; c0 < nch;
        c0 += stride) {
     u32x4 v[kAmaxU];
 #pragma unroll
     for (int u = 0; u < kAmaxU; ++u) {
-      const uint64_t c = c0 + (uint64_t)u * blockDim.x;
+      const uint64_t c = c0 + (uint64_t)u * kAmaxThreads;
       v[u] = c < nch ? ld(x + c) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -300,7 +333,7 @@ __global__ __launch_bounds__(256) void tw_amax_kernel(const u32x4 *__restrict__ 
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = part[0];
-    for (int i = 1; i < (int)(blockDim.x / kWave); ++i) r = r > part[i] ? r : part[i];
+    for (uint32_t i = 1; i < kAmaxThreads / kWave; ++i) r = r > part[i] ? r : part[i];
     atomicMax(slot, r);
   }
 }
@@ -312,8 +345,8 @@ __global__ __launch_bounds__(256) void tw_quantize_kernel(const u32x4 *__restric
                                                           uint64_t n, uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count();
-  const uint64_t w0 = wave_index();
+  const uint64_t nw = wave_count<4>();
+  const uint64_t w0 = wave_index<4>();
   const BlockScale b = block_scale<FMT>(*slot);
 
   for (uint64_t t = w0; t < full_tiles; t += nw) {
@@ -348,10 +381,10 @@ hipError_t launch_tw_t(const void *x, uint64_t n, void *q, float *scale, hipStre
   // number FP8Q_AMAX_WGS at most.  On MI355X (7 GB of bf16) 512-1024
   // workgroups read at ~7.0 TB/s, 4.5% faster than 2048 and 15% faster
   // than 256.
-  uint64_t wgs = (n / 8 + 256 * kAmaxU - 1) / (256 * kAmaxU);
+  uint64_t wgs = (n / 8 + kAmaxThreads * kAmaxU - 1) / (kAmaxThreads * kAmaxU);
   if (wgs > FP8Q_AMAX_WGS) wgs = FP8Q_AMAX_WGS;
   if (wgs < 1) wgs = 1;
-  hipLaunchKernelGGL(tw_amax_kernel, dim3((uint32_t)wgs), dim3(256), 0, stream,
+  hipLaunchKernelGGL(tw_amax_kernel, dim3((uint32_t)wgs), dim3(kAmaxThreads), 0, stream,
                      static_cast<const u32x4 *>(x), n, slot);
   const uint64_t full = n / ((uint64_t)U * kWave * 8);
   hipLaunchKernelGGL((tw_quantize_kernel<FMT, U>), dim3(grid_for_tiles(full)), dim3(256), 0, stream,

@@ -85,9 +85,13 @@ constexpr int peers_u() {
                 : (K <= 8 ? FP8Q_RED_U8 : (K <= 13 ? FP8Q_RED_U13 : FP8Q_RED_U16));
 }
 
+#ifndef FP8Q_RED_U8_BF16
+#define FP8Q_RED_U8_BF16 FP8Q_RED_U8   // tile depth for 4 < k <= 8 into bf16
+#endif
 template <int K, bool BF16 = false>
 constexpr int reduce_u() {
-  return K == 1 ? (BF16 ? FP8Q_RED_U1_BF16 : FP8Q_RED_U1) : peers_u<K>();
+  return K == 1 ? (BF16 ? FP8Q_RED_U1_BF16 : FP8Q_RED_U1)
+                : ((BF16 && K > 4 && K <= 8) ? FP8Q_RED_U8_BF16 : peers_u<K>());
 }
 
 template <int K, bool BF16 = false>
@@ -102,9 +106,26 @@ constexpr int reduce_t() {
 #ifndef FP8Q_XCD_CHUNK_DEQ
 #define FP8Q_XCD_CHUNK_DEQ 16
 #endif
-template <int K>
+#ifndef FP8Q_XCD_CHUNK_RED
+#define FP8Q_XCD_CHUNK_RED 16            // k-peer reduce into fp32: XCD run
+#endif
+#ifndef FP8Q_XCD_CHUNK_RED_BF16
+#define FP8Q_XCD_CHUNK_RED_BF16 64       // k-peer reduce into bf16: XCD run
+#endif
+#ifndef FP8Q_RED_WAVES
+#define FP8Q_RED_WAVES 4                 // k-peer reduce into fp32: waves per workgroup
+#endif
+#ifndef FP8Q_RED_WAVES_BF16
+#define FP8Q_RED_WAVES_BF16 1            // k-peer reduce into bf16: waves per workgroup
+#endif
+template <int K, bool BF16 = false>
+constexpr int reduce_waves() {
+  return (BF16 && K > 1 && K <= 8) ? FP8Q_RED_WAVES_BF16 : (K == 1 ? 4 : FP8Q_RED_WAVES);
+}
+template <int K, bool BF16 = false>
 constexpr int reduce_xcd_chunk() {
-  return K == 1 ? FP8Q_XCD_CHUNK_DEQ : FP8Q_XCD_CHUNK;
+  return K == 1 ? FP8Q_XCD_CHUNK_DEQ
+                : ((BF16 && K <= 8) ? FP8Q_XCD_CHUNK_RED_BF16 : FP8Q_XCD_CHUNK_RED);
 }
 
 // Non-temporal code loads pay off when several peers stream in; the single
@@ -247,12 +268,14 @@ __device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const TileIn<K, U
 // Each wave takes T consecutive tiles; the next tile's loads are issued
 // before the current tile's arithmetic.
 template <int FMT, int K, int U, int T, bool BF16>
-__global__ __launch_bounds__(256) void reduce_kernel(PeerPtrs P, void *__restrict__ y, uint64_t n,
-                                                     uint64_t full_tiles) {
+__global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
+    PeerPtrs P, void *__restrict__ y, uint64_t n, uint64_t full_tiles) {
+  constexpr int W = reduce_waves<K, BF16>();
+  constexpr int C = reduce_xcd_chunk<K, BF16>();
   constexpr uint64_t kTile = (uint64_t)U * 256;
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count<4>();
-  const uint64_t w0 = wave_index<4, reduce_xcd_chunk<K>()>();
+  const uint64_t nw = wave_count<W>();
+  const uint64_t w0 = wave_index<W, C>();
 
   constexpr bool VS = kRedVecScales<K>;
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
@@ -278,8 +301,10 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
   constexpr int T = reduce_t<K, BF16>();
   const uint64_t tile = (uint64_t)U * 256;
   const uint64_t full = n / tile;
-  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
-                     dim3(256), 0, stream, P, y, n, full);
+  constexpr int W = reduce_waves<K, BF16>();
+  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>),
+                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P, y,
+                     n, full);
   return hipGetLastError();
 }
 

@@ -24,8 +24,9 @@
 // where scalar registers run short, through vector loads issued with the
 // codes).  Codes are decoded by
 // the hardware packed FP8->fp32 conversion.  The dequantized values live
-// only in registers.  The file also holds the requantize variant and the
-// MXFP8 receiver, which share this mapping.
+// only in registers.  The file also holds the MXFP8 receiver, which shares
+// this mapping, and the reduce -> requantize, which holds eight codes per
+// lane so that a block is one 16-lane row.
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -183,22 +184,15 @@ __device__ void reduce_tail(const PeerPtrs &P, void *__restrict__ y, uint64_t n,
 // shards, bf16 out): at U = 1, vector scales are 3-7% faster than the scalar
 // path for 9 and 10 peers, even at 11 and slower at 12 and 13; for 14..16
 // peers U = 2 on the scalar path is fastest (about 30% over U = 1, whose
-// scalar registers spill).  The requantize, whose block amax and scale math
-// need scalar registers too, is 4-8% faster with vector scales from 2 peers
-// up and about 30% faster at 16 peers with U = 2.
+// scalar registers spill).  The requantize loads its scales per lane too.
 #ifndef FP8Q_RED_VSCALE_MIN
 #define FP8Q_RED_VSCALE_MIN 9
 #endif
 #ifndef FP8Q_RED_VSCALE_MAX
 #define FP8Q_RED_VSCALE_MAX 11
 #endif
-#ifndef FP8Q_RQ_VSCALE_K
-#define FP8Q_RQ_VSCALE_K 2
-#endif
 template <int K>
 constexpr bool kRedVecScales = K >= FP8Q_RED_VSCALE_MIN && K <= FP8Q_RED_VSCALE_MAX;
-template <int K>
-constexpr bool kRqVecScales = K >= FP8Q_RQ_VSCALE_K;
 
 // One tile's inputs in registers: codes, and (vector-scale mode VS) scales.
 template <int K, int U, bool VS>
@@ -295,8 +289,40 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
   if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
 }
 
+// The reduce into bf16 from FP8Q_RED8_MIN_K_BF16 peers up holds eight codes
+// per lane (reduce8_kernel): U = 1 group of 512 elements per tile, T = 2
+// tiles per wave, 4-wave workgroups, XCD runs of 16.  Each wave instruction
+// reads 512 B of a peer's codes, so the loads per element halve, and the
+// bf16 result leaves as one 16-byte store per lane (1 KiB per instruction).
+// Measured on MI355X against reduce_kernel, alternated in one run (% of
+// 8 TB/s at 437.5 MiB / 64 MiB per peer): k = 12 81.8 / 80.0 against
+// 78.6 / 75.6; k = 16 80.0 / 80.0 against 76.7 / 71.6.  Up to 8 peers it
+// was no faster (k = 8: 82.5 / 77.8 against 83.3 / 78.8), and into fp32,
+// whose 32 bytes per lane leave as two stores at a 32-byte stride, it was
+// 10-45% slower at every peer count, so those keep reduce_kernel.
+#ifndef FP8Q_RED8_MIN_K_BF16
+#define FP8Q_RED8_MIN_K_BF16 9
+#endif
+#ifndef FP8Q_RED8_U
+#define FP8Q_RED8_U 1
+#endif
+#ifndef FP8Q_RED8_T
+#define FP8Q_RED8_T 2
+#endif
+#ifndef FP8Q_RED8_W
+#define FP8Q_RED8_W 4
+#endif
+#ifndef FP8Q_RED8_C
+#define FP8Q_RED8_C 16
+#endif
+
+template <int FMT, int K, bool BF16>
+hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream);
+
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
+  if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_BF16)
+    return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
   constexpr int U = reduce_u<K, BF16>();
   constexpr int T = reduce_t<K, BF16>();
   const uint64_t tile = (uint64_t)U * 256;
@@ -339,10 +365,6 @@ hipError_t dispatch_k(int k, const PeerPtrs &P, uint64_t n, void *y, hipStream_t
 // intermediate could leave the normal range the quotient is below 2^-26, far
 // under half the smallest FP8 subnormal, and the sequence keeps the
 // dividend's sign, so the code is the same signed zero.
-//
-// Same mapping as reduce_kernel: lanes 0-31 of a 256-element group hold one
-// block, lanes 32-63 the next; the block amax is 4 DPP steps within each
-// 16-lane row plus one swap of rows 0<->1 and 2<->3.
 
 __device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 
@@ -411,144 +433,226 @@ __device__ void requant_tail(const PeerPtrs &P, uint8_t *__restrict__ qo, float 
   }
 }
 
-// Requantize tile shape, by peer count (measured on MI355X).  U = 2 at every
-// k: at k = 9..12 it beats the reduce's U = 1 by 11-18% (3 waves per SIMD
-// instead of 4, but twice the loads in flight per wave).  T = 4 tiles per
-// wave, except at k = 9..12 where T = 2 measured 2-3% faster; T = 4 beat
-// T = 2 by 5-10% at k = 1..4 and tied at k = 8 and 14..16.  T = 3, 6 and 8,
-// U = 1 and scalar input scales were slower.
-#ifndef FP8Q_RQ_U
-#define FP8Q_RQ_U 0              // requantize tile depth; 0: by k as below
-#endif
-#ifndef FP8Q_RQ_T
-#define FP8Q_RQ_T 0              // requantize tiles per wave; 0: by k as below
-#endif
-template <int K>
-constexpr int requant_u() {
-  return FP8Q_RQ_U > 0 ? FP8Q_RQ_U : 2;
-}
-template <int K>
-constexpr int requant_t() {
-  return FP8Q_RQ_T > 0 ? FP8Q_RQ_T : (K >= 9 && K <= 12 ? 2 : 4);
+// Mapping: eight codes per lane.  A lane holds elements [8 lane, 8 lane + 8)
+// of each 512-element group (8-byte code loads, 512 B per wave instruction
+// and peer), so a 128-element block is one 16-lane DPP row, exactly as in
+// the bf16 quantize: its amax is a max over the lane's 8 sums and 4 DPP
+// steps (no cross-row exchange), and each lane's block scale and reciprocal
+// serve 8 elements.  Each lane loads its block's input scale per peer (16
+// lanes share the address).  The codes leave as 8-byte stores (512 B per
+// instruction); the tile's 4U output scales are staged in LDS and leave in
+// one contiguous store per workgroup round.  Where the block amax and scale
+// arithmetic, rather than HBM, bind the kernel (few peers), this halves
+// their cost per element against a mapping with four codes per lane.
+
+template <int K, int U>
+struct Tile8 {
+  u32x2 w[K][U];
+  float s[K][U];
+};
+
+template <int K, int U>
+__device__ __forceinline__ void load_tile8(const PeerPtrs &P, uint64_t t, uint32_t lane,
+                                           Tile8<K, U> &in) {
+  const uint64_t e0 = t * ((uint64_t)U * 512) + 8u * lane;   // lane's first element of tile t
+#pragma unroll
+  for (int p = 0; p < K; ++p)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t e = e0 + (uint64_t)u * 512;
+      in.w[p][u] = ld<u32x2, kNtCodes<K>>(reinterpret_cast<const u32x2 *>(P.q[p]) + e / 8);
+      in.s[p][u] = ld<float, false>(P.s[p] + e / kBlock);
+    }
 }
 
-// One tile: sum, requantize, store the codes, and put the tile's 2U scales
-// at s_dst[0 .. 2U) in the workgroup's LDS staging array.
-template <int FIN, int FOUT, int K, int U, bool VS>
-__device__ __forceinline__ void requant_tile(const PeerPtrs &P, const TileIn<K, U, VS> &in,
-                                             uint32_t *__restrict__ qo, float *s_dst,
-                                             uint64_t t, uint32_t lane) {
-  constexpr uint64_t kTile = (uint64_t)U * 256;
-  const bool upper = lane >= 32;
-  const uint64_t dw0 = t * (kTile / 4);
-  float acc[U][4];
-  sum_tile<FIN, K, U, VS>(P, in, t, lane, acc);
+template <int FMT, int K, int U>
+__device__ __forceinline__ void sum_tile8(const Tile8<K, U> &in, float (&acc)[U][8]) {
+#pragma unroll
+  for (int p = 0; p < K; ++p)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float s = in.s[p][u];
+      const f32x2 a = dec2<FMT, false>(in.w[p][u].x), b = dec2<FMT, true>(in.w[p][u].x);
+      const f32x2 c = dec2<FMT, false>(in.w[p][u].y), d = dec2<FMT, true>(in.w[p][u].y);
+      const float v[8] = {a[0] * s, a[1] * s, b[0] * s, b[1] * s,
+                          c[0] * s, c[1] * s, d[0] * s, d[1] * s};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[u][j] = (p == 0) ? v[j] : acc[u][j] + v[j];
+    }
+}
+
+template <int FOUT, bool SCALED>
+__device__ __forceinline__ u32x2 quot8(const float (&a)[8], const F32Scale &sc) {
+  return u32x2{cvt4<FOUT>(f32_quot<FOUT, SCALED>(a[0], sc), f32_quot<FOUT, SCALED>(a[1], sc),
+                          f32_quot<FOUT, SCALED>(a[2], sc), f32_quot<FOUT, SCALED>(a[3], sc)),
+               cvt4<FOUT>(f32_quot<FOUT, SCALED>(a[4], sc), f32_quot<FOUT, SCALED>(a[5], sc),
+                          f32_quot<FOUT, SCALED>(a[6], sc), f32_quot<FOUT, SCALED>(a[7], sc))};
+}
+
+// One tile: sum, requantize, store the codes, and put the tile's 4U scales at
+// s_dst[0 .. 4U) (block u * 4 + row of the tile).
+template <int FIN, int FOUT, int K, int U>
+__device__ __forceinline__ void requant8_tile(const Tile8<K, U> &in, u32x2 *__restrict__ qo,
+                                              float *s_dst, uint64_t t, uint32_t lane) {
+  const uint32_t row = lane >> 4, col = lane & 15;
+  float acc[U][8];
+  sum_tile8<FIN, K, U>(in, acc);
+  float sc_s[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     uint32_t m = abs_bits(acc[u][0]);
 #pragma unroll
-    for (int j = 1; j < 4; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
-    const F32Scale sc = f32_block_scale<FOUT>(max_half32(m));
-    uint32_t c;
-    // x' = v * f only where a block of this load needs it (amax < 2^-60):
-    // skipping the multiply measured 4-8% faster for k <= 4
-    if (wave_any(sc.f != 1.0f))
-      c = cvt4<FOUT>(f32_quot<FOUT, true>(acc[u][0], sc), f32_quot<FOUT, true>(acc[u][1], sc),
-                     f32_quot<FOUT, true>(acc[u][2], sc), f32_quot<FOUT, true>(acc[u][3], sc));
-    else
-      c = cvt4<FOUT>(f32_quot<FOUT, false>(acc[u][0], sc), f32_quot<FOUT, false>(acc[u][1], sc),
-                     f32_quot<FOUT, false>(acc[u][2], sc), f32_quot<FOUT, false>(acc[u][3], sc));
-    if (!sc.finite) c = 0x7F7F7F7Fu;
-    st(qo + dw0 + u * kWave + lane, c);
-    if ((lane & 31) == 0) s_dst[2 * u + (upper ? 1 : 0)] = sc.s;
+    for (int j = 1; j < 8; ++j) m = m > abs_bits(acc[u][j]) ? m : abs_bits(acc[u][j]);
+    const F32Scale sc = f32_block_scale<FOUT>(max_row16(m));
+    u32x2 c = wave_any(sc.f != 1.0f) ? quot8<FOUT, true>(acc[u], sc) : quot8<FOUT, false>(acc[u], sc);
+    if (!sc.finite) c = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+    st(qo + t * ((uint64_t)U * 64) + (uint64_t)u * 64 + lane, c);
+    sc_s[u] = sc.s;
+  }
+  // lane (row, col = u) writes block u * 4 + row: one LDS write covers the tile
+  if (col < U) {
+    float s = sc_s[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) s = (col == (uint32_t)u) ? sc_s[u] : s;
+    s_dst[col * 4 + row] = s;
   }
 }
 
-// A wave's T consecutive tiles [t0, t0 + T) (those below full_tiles), the
-// next tile's loads issued first; tile t0 + j puts its scales at
-// s_dst + 2U * j.
+// A wave's T consecutive tiles, the next tile's loads issued first; tile
+// t0 + j puts its scales at s_dst + 4U * j.
 template <int FIN, int FOUT, int K, int U, int T>
-__device__ __forceinline__ void requant_wave_tiles(const PeerPtrs &P, uint32_t *__restrict__ qo,
-                                                   float *s_dst, uint64_t t0, uint64_t full_tiles,
-                                                   uint32_t lane) {
-  constexpr bool VS = kRqVecScales<K>;
-  TileIn<K, U, VS> cur;
-  load_tile<K, U, VS>(P, t0, lane, cur);
+__device__ __forceinline__ void requant8_wave_tiles(const PeerPtrs &P, u32x2 *__restrict__ qo,
+                                                    float *s_dst, uint64_t t0,
+                                                    uint64_t full_tiles, uint32_t lane) {
+  Tile8<K, U> cur;
+  load_tile8<K, U>(P, t0, lane, cur);
 #pragma unroll
   for (int j = 0; j < T; ++j) {
     const uint64_t t = t0 + j;
     if (t >= full_tiles) break;
-    TileIn<K, U, VS> nxt;
+    Tile8<K, U> nxt;
     const bool more = (j + 1 < T) && (t + 1 < full_tiles);
-    if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
-    requant_tile<FIN, FOUT, K, U, VS>(P, cur, qo, s_dst + 2 * U * j, t, lane);
+    if (more) load_tile8<K, U>(P, t + 1, lane, nxt);
+    requant8_tile<FIN, FOUT, K, U>(cur, qo, s_dst + 4 * U * j, t, lane);
     if (more) cur = nxt;
   }
 }
 
-// T consecutive tiles per wave.  The workgroup's 4T tiles stage their 8UT
-// scales in LDS, and they leave in one contiguous store rather than as 8UT
-// four-byte stores from different waves (measured 2.7% faster for k = 8).
 template <int FIN, int FOUT, int K, int U, int T, int W, int C>
-__global__ __launch_bounds__(64 * W) void requant_kernel(PeerPtrs P, uint32_t *__restrict__ qo,
-                                                         float *__restrict__ so, uint64_t n,
-                                                         uint64_t full_tiles) {
-  constexpr uint64_t kTile = (uint64_t)U * 256;
-  constexpr uint32_t kTileBlocks = 2 * U;
-  constexpr uint32_t kWgTiles = W * T;             // W waves per workgroup
+__global__ __launch_bounds__(64 * W) void requant8_kernel(PeerPtrs P, u32x2 *__restrict__ qo,
+                                                          float *__restrict__ so, uint64_t n,
+                                                          uint64_t full_tiles) {
+  constexpr uint64_t kTile = (uint64_t)U * 512;
+  constexpr uint32_t kTileBlocks = 4 * U;
   const uint32_t lane = lane_id();
-  const uint64_t nw = wave_count<W>();
-  const uint64_t w0 = wave_index<W, C>();
-
-  __shared__ float wg_scales[kWgTiles * kTileBlocks];
+  __shared__ float wg_scales[W * T * kTileBlocks];
   workgroup_rounds<T, W, C>(
       full_tiles,
       [&](uint64_t t0, uint32_t wid) {
-        requant_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
-                                               full_tiles, lane);
+        requant8_wave_tiles<FIN, FOUT, K, U, T>(P, qo, wg_scales + wid * T * kTileBlocks, t0,
+                                                full_tiles, lane);
       },
       [&](uint64_t base, uint32_t tiles) {
         for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
           so[base * kTileBlocks + i] = wg_scales[i];
       });
-  if (w0 == nw - 1)
+  if (wave_index<W, C>() == wave_count<W>() - 1)
     requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
 }
 
-// Workgroup shape.  4 waves per workgroup (XCD runs of FP8Q_XCD_CHUNK),
-// except for 13 or more peers on at least FP8Q_RQ_WIDE_N elements: there
-// the kernel holds 178-216 VGPRs, 2 waves per SIMD, and a 4-wave workgroup's
-// barrier before the scale flush stalls a large share of the CU; one-wave
-// workgroups (XCD runs of 256, the same bytes per run) measured 1-3% faster
-// at k = 16 for 16 - 256 MiB payloads on MI355X and 8% faster on
-// 218.75M-element shards, but 2% slower at 4 MiB.  For fewer peers the two
-// shapes were within +-2%.
-#ifndef FP8Q_RQ_WIDE_N
-#define FP8Q_RQ_WIDE_N (1ull << 23)
+// Tile shape: U = 2 groups of 512 elements per tile, T = 2 tiles per wave,
+// 4-wave workgroups, at every peer count.  Against the previous requantize
+// (four codes per lane, a block across 32 lanes, its tile shape tuned per
+// peer count), measured on MI355X with the variants alternated in one run
+// (graph replay over rotating windows, % of 8 TB/s at 437.5 MiB / 64 MiB per
+// peer): k = 1 75 / 58 against 58 / 48; k = 8 80 / 76 against 78 / 69;
+// k = 12 76 / 76 against 70 / 68.5; k = 16 75.5 / 78 against 75 / 71; k = 4
+// 81.5 / 74 against 82 / 71.5.  T = 4 was slower, and so was U = 1 from 9
+// peers up (7-10%), although it halves the registers (k >= 12 holds 256
+// VGPRs, one wave per SIMD, with 32 KiB of codes in flight per wave).
+#ifndef FP8Q_RQ8_U
+#define FP8Q_RQ8_U 2             // 512-element groups per tile
 #endif
-#ifndef FP8Q_RQ_WIDE_K
-#define FP8Q_RQ_WIDE_K 13
+template <int K>
+constexpr int requant8_u() {
+  return FP8Q_RQ8_U;
+}
+#ifndef FP8Q_RQ8_T
+#define FP8Q_RQ8_T 2             // tiles per wave
+#endif
+// XCD runs of 16 workgroups: against 64 they measured 1.5-3% faster at
+// 437.5 MiB per peer for 2-16 peers and on the 8 x 437.5M-element gradient
+// shards (80.1% against 78.4%), about 1% slower at 64 MiB from 8 peers up.
+#ifndef FP8Q_XCD_CHUNK_RQ
+#define FP8Q_XCD_CHUNK_RQ 16     // XCD run (workgroups) of the requantize
 #endif
 
-template <int FIN, int FOUT, int K, int W, int C>
-void launch_requant_shape(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
-  constexpr int U = requant_u<K>();
-  constexpr int T = requant_t<K>();
-  const uint64_t full = n / ((uint64_t)U * 256);
-  hipLaunchKernelGGL((requant_kernel<FIN, FOUT, K, U, T, W, C>),
+template <int FIN, int FOUT, int K>
+void launch_requant8(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
+  constexpr int U = requant8_u<K>();
+  constexpr int T = FP8Q_RQ8_T;
+  constexpr int W = 4;
+  const uint64_t full = n / ((uint64_t)U * 512);
+  hipLaunchKernelGGL((requant8_kernel<FIN, FOUT, K, U, T, W, FP8Q_XCD_CHUNK_RQ>),
                      dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P,
-                     static_cast<uint32_t *>(qo), so, n, full);
+                     static_cast<u32x2 *>(qo), so, n, full);
+}
+
+// The k-peer reduce with eight codes per lane: the requantize's mapping and
+// tile loads, then the ordered sum stored as fp32 or bf16 (see launch_reduce_t
+// for which peer counts and outputs take it).
+template <bool BF16>
+__device__ __forceinline__ void store8(void *y, uint64_t e, const float (&a)[8]) {
+  if constexpr (BF16) {
+    st(reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y) + e),
+       u32x4{bf16_pack2(a[0], a[1]), bf16_pack2(a[2], a[3]), bf16_pack2(a[4], a[5]),
+             bf16_pack2(a[6], a[7])});
+  } else {
+    st(reinterpret_cast<f32x4 *>(static_cast<float *>(y) + e), f32x4{a[0], a[1], a[2], a[3]});
+    st(reinterpret_cast<f32x4 *>(static_cast<float *>(y) + e + 4), f32x4{a[4], a[5], a[6], a[7]});
+  }
+}
+
+template <int FMT, int K, int U, int T, bool BF16, int W, int C>
+__global__ __launch_bounds__(64 * W) void reduce8_kernel(PeerPtrs P, void *__restrict__ y,
+                                                         uint64_t n, uint64_t full_tiles) {
+  constexpr uint64_t kTile = (uint64_t)U * 512;
+  const uint32_t lane = lane_id();
+  const uint64_t nw = wave_count<W>();
+  const uint64_t w0 = wave_index<W, C>();
+  for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
+    Tile8<K, U> cur;
+    load_tile8<K, U>(P, t0, lane, cur);
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      const uint64_t t = t0 + j;
+      if (t >= full_tiles) break;
+      Tile8<K, U> nxt;
+      const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+      if (more) load_tile8<K, U>(P, t + 1, lane, nxt);
+      float acc[U][8];
+      sum_tile8<FMT, K, U>(cur, acc);
+#pragma unroll
+      for (int u = 0; u < U; ++u) store8<BF16>(y, t * kTile + (uint64_t)u * 512 + 8u * lane, acc[u]);
+      if (more) cur = nxt;
+    }
+  }
+  if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
+}
+
+template <int FMT, int K, bool BF16>
+hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
+  constexpr int U = FP8Q_RED8_U, T = FP8Q_RED8_T, W = FP8Q_RED8_W;
+  const uint64_t full = n / ((uint64_t)U * 512);
+  hipLaunchKernelGGL((reduce8_kernel<FMT, K, U, T, BF16, W, FP8Q_RED8_C>),
+                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P, y,
+                     n, full);
+  return hipGetLastError();
 }
 
 template <int FIN, int FOUT, int K>
 hipError_t launch_requant_t(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
-  if constexpr (K >= FP8Q_RQ_WIDE_K) {
-    if (n >= FP8Q_RQ_WIDE_N) {
-      launch_requant_shape<FIN, FOUT, K, 1, 256>(P, n, qo, so, stream);
-      return hipGetLastError();
-    }
-  }
-  launch_requant_shape<FIN, FOUT, K, 4, FP8Q_XCD_CHUNK>(P, n, qo, so, stream);
+  launch_requant8<FIN, FOUT, K>(P, n, qo, so, stream);
   return hipGetLastError();
 }
 

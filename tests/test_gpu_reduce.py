@@ -121,6 +121,25 @@ def test_ragged_sizes_leave_canaries(n):
     assert np.all(ybh[n:] == 77)
 
 
+@pytest.mark.parametrize("k", [9, 16])
+@pytest.mark.parametrize("n", [1, 127, 511, 512, 513, 1025, 4096 + 77])
+def test_many_peers_bf16_ragged_sizes_leave_canaries(k, n):
+    """From 9 peers up the reduce into bf16 maps eight codes to a lane
+    (512-element tiles); around and below one tile only the tail path runs."""
+    dev = require_gpu()
+    shards = [workloads.random_wire_shard(n, seed=7 * n + p, fmt=1) for p in range(k)]
+    qs = [dev_u8(a.numpy(), dev) for a, _ in shards]
+    ss = [dev_f32(b.numpy(), dev) for _, b in shards]
+    yb_big = torch.full((n + 40,), 77, dtype=torch.int16, device=dev)
+    fq.fp8q_dequant_reduce(qs, ss, 1, out_dtype=torch.bfloat16, out=yb_big.view(torch.bfloat16)[:n])
+    torch.cuda.synchronize()
+    ybh = host(yb_big)
+    want = oracle.dequant_reduce([a.numpy() for a, _ in shards], [b.numpy() for _, b in shards], 1,
+                                 out_bf16=True)
+    assert_bf16_parity(ybh[:n].view(np.uint16), want, "bf16 k=%d n=%d" % (k, n))
+    assert np.all(ybh[n:] == 77)
+
+
 @pytest.mark.parametrize("nbytes", workloads.SWEEP_BYTES)
 def test_payload_sweep_e5m2_k8(nbytes):
     dev = require_gpu()

@@ -689,6 +689,74 @@ def stress_reduce(torch, fq, workloads, dev, reps=21):
     return res
 
 
+def mid_size_only(torch, fq, workloads, dev, reps):
+    """The gated mid-size dispatches alone, each launched eagerly `reps`
+    times on rotating inputs and timed with HIP events on the current
+    stream (no HIP graphs, so that a profiler sees ordinary dispatches):
+    the 64 MiB payload's e5m2 and e4m3 quantize and its k = 8 reduce into
+    fp32, the full stress payload's k = 8 reduce into bf16 (e4m3, e5m2), and
+    the k = 16 reduce into bf16 of 218,750,000-element peers.  Returns one
+    record per op: mean, median and minimum launch time, and % of peak."""
+    res = {}
+
+    def timed(name, fns, alg_bytes):
+        for f in fns[:2]:
+            f()
+        torch.cuda.synchronize()
+        ev = []
+        for f in fns:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        mean = sum(us) / len(us)
+        res[name] = {"us": round(mean, 2), "us_median": round(us[len(us) // 2], 2),
+                     "us_min": round(us[0], 2), "hbm_GBps": round(alg_bytes / mean / 1e3, 1),
+                     "frac_peak": round(alg_bytes / mean / 1e3 / HBM_PEAK_GBS, 4)}
+
+    # 64 MiB payload: windows of a 2 GiB bf16 pool, 8 peers for the reduce
+    n_pool, n = 1 << 30, (64 << 20) // 2
+    x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)
+    q = torch.empty(n_pool, dtype=torch.uint8, device=dev)
+    s = torch.empty(n_pool // 128, dtype=torch.float32, device=dev)
+    fq.fp8q_quantize(x, fq.E5M2, q_out=q, scales_out=s)
+    y = torch.empty(4 * n, dtype=torch.float32, device=dev)
+    win = [(i * 9 * n) % (n_pool - 9 * n) // 128 * 128 for i in range(reps)]
+    for fmt, name in ((fq.E5M2, "quantize_e5m2_64MiB"), (fq.E4M3, "quantize_e4m3_64MiB")):
+        timed(name, [lambda o=o, fmt=fmt: fq.fp8q_quantize(
+            x[o:o + n], fmt, q_out=q[o:o + n], scales_out=s[o // 128:o // 128 + n // 128])
+            for o in win], QUANT_BYTES_PER_ELEM * n)
+    fq.fp8q_quantize(x, fq.E5M2, q_out=q, scales_out=s)
+    timed("reduce_k8_f32_64MiB", [lambda o=o, i=i: fq.fp8q_dequant_reduce(
+        [q[o + p * n:o + (p + 1) * n] for p in range(8)],
+        [s[(o + p * n) // 128:(o + (p + 1) * n) // 128] for p in range(8)], fq.E5M2,
+        out=y[(i % 4) * n:(i % 4 + 1) * n]) for i, o in enumerate(win)],
+        reduce_bytes_per_elem(8, 4) * n)
+    del x, q, s, y
+    # the stress payload's full k = 8 reduce into bf16, 7 copies rotating
+    ns = workloads.STRESS_N
+    for fmt, name in ((fq.E4M3, "stress_reduce_k8_bf16_e4m3"), (fq.E5M2, "stress_reduce_k8_bf16_e5m2")):
+        sets = [([workloads.random_wire_shard(ns, seed=300 + p, fmt=fmt, device=dev)
+                  for p in range(8)], torch.empty(ns, dtype=torch.bfloat16, device=dev))
+                for _ in range(7)]
+        timed(name, [lambda c=sets[i % 7], fmt=fmt: fq.fp8q_dequant_reduce(
+            [a for a, _ in c[0]], [b for _, b in c[0]], fmt, out_dtype=torch.bfloat16, out=c[1])
+            for i in range(reps)], reduce_bytes_per_elem(8, 2) * ns)
+        del sets
+    # k = 16 into bf16: 16 peers of 218,750,000 elements, two output buffers
+    nk = 218_750_000
+    peers = [workloads.random_wire_shard(nk, seed=400 + p, fmt=fq.E4M3, device=dev) for p in range(16)]
+    outs = [torch.empty(nk, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    timed("reduce_k16_bf16_218.75M", [lambda i=i: fq.fp8q_dequant_reduce(
+        [a for a, _ in peers], [b for _, b in peers], fq.E4M3, out_dtype=torch.bfloat16,
+        out=outs[i % 2]) for i in range(reps)], reduce_bytes_per_elem(16, 2) * nk)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -700,6 +768,9 @@ def main():
     ap.add_argument("--no-side", action="store_true", help="skip the naive-path side figures")
     ap.add_argument("--copy-reference-gib", type=float, default=1.0,
                     help="size of the plain device copy run once for counter calibration")
+    ap.add_argument("--mid-size-only", action="store_true",
+                    help="run only the gated mid-size dispatches, eagerly (for profiling); "
+                         "prints their timings as one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -714,6 +785,19 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mid_size_only:
+        if args.copy_reference_gib > 0:
+            nb = int(args.copy_reference_gib * (1 << 30))
+            src = torch.empty(nb, dtype=torch.uint8, device=dev)
+            src.fill_(1)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
+        log("mid-size dispatches, %d launches each" % args.steps)
+        print(json.dumps({"mid_size_only": True, "steps": args.steps,
+                          "ops": mid_size_only(torch, fq, workloads, dev, args.steps),
+                          "env": device_info(torch, dev)}), flush=True)
+        return
     fmt = fq.E4M3
     n = workloads.PI05_N
     k = workloads.PI05_PEERS

@@ -316,6 +316,15 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
 #define FP8Q_RED8_C 16
 #endif
 
+// Dynamic LDS the single-shard dequantize into bf16 reserves per workgroup
+// (the kernel uses none), so that at most 6 of its 4-wave workgroups share a
+// CU: 437.5M elements took 206.5-207.8 us capped against 212.7-213.9 us
+// uncapped (80.0% against 77.7% of 8 TB/s, alternated in one run on
+// MI355X); into fp32 the cap moved it within noise, so that keeps none.
+#ifndef FP8Q_DEQ_BF16_LDS
+#define FP8Q_DEQ_BF16_LDS 24576
+#endif
+
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream);
 
@@ -329,8 +338,8 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
   const uint64_t full = n / tile;
   constexpr int W = reduce_waves<K, BF16>();
   hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>),
-                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P, y,
-                     n, full);
+                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W),
+                     (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0, stream, P, y, n, full);
   return hipGetLastError();
 }
 

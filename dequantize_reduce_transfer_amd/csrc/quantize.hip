@@ -166,6 +166,17 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #define FP8Q_QUANT_LDS_PAD_W4 21504
 #endif
 
+// The same for the one-wave workgroups of large payloads: 5.5 KiB each, so
+// that about 28 share a CU instead of 32.  On MI355X (alternated in one run)
+// the 3.5e9-element quantize took 1552-1557 us capped against 1590 us
+// uncapped (85.3% against 83.4% of 8 TB/s), 1 GiB 240 against 244-249 us and
+// 512 MiB 122 against 124 us; caps of 24 and 26 were within 0.5% of 28, 16
+// was no faster than none, and without the store wait before the scale
+// flush the capped kernel was 0.5% slower.
+#ifndef FP8Q_QUANT_LDS_PAD_W1
+#define FP8Q_QUANT_LDS_PAD_W1 5632
+#endif
+
 // One tile: quantize the U loaded chunks, store the codes, and put the
 // tile's 4U scales at sc_dst[0 .. 4U) in the workgroup's LDS staging array.
 template <int FMT, int U>
@@ -233,7 +244,8 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
                                                           uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
   constexpr uint32_t kTileBlocks = 4 * U;
-  __shared__ float wg_scales[W * T * kTileBlocks + (W == 4 ? FP8Q_QUANT_LDS_PAD_W4 / 4 : 0)];
+  __shared__ float wg_scales[W * T * kTileBlocks + (W == 4 ? FP8Q_QUANT_LDS_PAD_W4 / 4
+                                                            : FP8Q_QUANT_LDS_PAD_W1 / 4)];
   const uint32_t lane = lane_id();
   workgroup_rounds<T, W, C>(
       full_tiles,

@@ -26,7 +26,8 @@
 // workgroup's LDS staging array, from which they leave in one contiguous
 // store per workgroup.  Each wave takes T consecutive tiles, issuing the
 // next tile's loads before the current tile's arithmetic; the grid has one
-// wave per T tiles, placed XCD-aware.
+// wave per T tiles, placed XCD-aware, in 4-wave workgroups, or one-wave
+// workgroups on large tensors (see FP8Q_MX8_WIDE_N).
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -76,7 +77,19 @@ __device__ __forceinline__ u32x2 mx_quant8(u32x4 v, const MxScale &m) {
   return r;
 }
 
-constexpr int kWgWaves = 4;                      // waves per 256-thread workgroup
+// Workgroup shape by size, as for the block quantize: from FP8Q_MX8_WIDE_N
+// elements a workgroup is one wave (XCD runs of 256), it waits for its code
+// stores before each round's E8M0 flush, and it asks for 5.5 KiB of dynamic
+// LDS so that about 28 share a CU; below that, 4-wave workgroups in XCD runs
+// of 64.  On the MoE layer's 201M-element tensors (MI355X, five alternated
+// rounds) the one-wave shape took 92.1-93.1 us against 93.2-94.3 us (82.4%
+// against 81.4% of 8 TB/s on average).
+#ifndef FP8Q_MX8_WIDE_N
+#define FP8Q_MX8_WIDE_N (1ull << 27)
+#endif
+#ifndef FP8Q_MX8_W1_LDS
+#define FP8Q_MX8_W1_LDS 5632
+#endif
 
 // One tile: quantize, store the codes, and put the tile's 16U E8M0 bytes at
 // e_dst[0 .. 16U) in the workgroup's LDS staging array.
@@ -134,34 +147,36 @@ __device__ __forceinline__ void mx_wave_tiles(const u32x4 *__restrict__ w, u32x2
 // their E8M0 bytes in LDS, and they leave in one contiguous store (whole
 // 128-byte lines: 4-byte stores when the scale pointer allows, else bytes)
 // rather than as 4T partial-line byte stores from different waves.
-template <int U, int T>
-__global__ __launch_bounds__(256) void mx8_kernel(const u32x4 *__restrict__ w, u32x2 *__restrict__ q,
-                                                  uint8_t *__restrict__ e8m0, uint64_t nchunks,
-                                                  uint64_t full_tiles) {
+template <int U, int T, int W, int C>
+__global__ __launch_bounds__(64 * W) void mx8_kernel(const u32x4 *__restrict__ w,
+                                                     u32x2 *__restrict__ q,
+                                                     uint8_t *__restrict__ e8m0, uint64_t nchunks,
+                                                     uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
   constexpr uint32_t kTileBytes = 16 * U;          // E8M0 bytes per tile
-  constexpr uint32_t kWgTiles = kWgWaves * T;
+  constexpr uint32_t kWgTiles = W * T;
   const uint32_t lane = lane_id();
   const uint32_t c = lane & 3;
-  const uint64_t nw = wave_count<kWgWaves>();
-  const uint64_t w0 = wave_index<kWgWaves>();
+  const uint64_t nw = wave_count<W>();
+  const uint64_t w0 = wave_index<W, C>();
 
   __shared__ uint32_t wg_e8m0[kWgTiles * kTileBytes / 4];
   uint8_t *stage = reinterpret_cast<uint8_t *>(wg_e8m0);
   const bool words = (reinterpret_cast<uintptr_t>(e8m0) & 3u) == 0;
-  workgroup_rounds<T>(
+  workgroup_rounds<T, W, C>(
       full_tiles,
       [&](uint64_t t0, uint32_t wid) {
         mx_wave_tiles<U, T>(w, q, stage + wid * T * kTileBytes, t0, full_tiles, lane);
       },
       [&](uint64_t base, uint32_t tiles) {
+        if constexpr (W == 1) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         const uint32_t nb = tiles * kTileBytes;
         uint8_t *dst = e8m0 + base * kTileBytes;
         if (words) {
-          for (uint32_t i = threadIdx.x; i < nb / 4; i += 64 * kWgWaves)
+          for (uint32_t i = threadIdx.x; i < nb / 4; i += 64 * W)
             reinterpret_cast<uint32_t *>(dst)[i] = wg_e8m0[i];
         } else {
-          for (uint32_t i = threadIdx.x; i < nb; i += 64 * kWgWaves) dst[i] = stage[i];
+          for (uint32_t i = threadIdx.x; i < nb; i += 64 * W) dst[i] = stage[i];
         }
       });
   // Tail: whole blocks only (the element count is a multiple of 32, so every
@@ -188,10 +203,14 @@ hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0,
   constexpr int T = kMxT;
   const uint64_t nchunks = n / 8;
   const uint64_t full = nchunks / ((uint64_t)U * kWave);
-  hipLaunchKernelGGL((mx8_kernel<U, T>), dim3(grid_for_tiles((full + T - 1) / T)), dim3(256), 0,
-                     stream,
-                     static_cast<const u32x4 *>(w), static_cast<u32x2 *>(q),
-                     static_cast<uint8_t *>(e8m0), nchunks, full);
+  if (n >= FP8Q_MX8_WIDE_N)
+    hipLaunchKernelGGL((mx8_kernel<U, T, 1, 256>), dim3(grid_for_tiles((full + T - 1) / T, 1)),
+                       dim3(64), FP8Q_MX8_W1_LDS, stream, static_cast<const u32x4 *>(w),
+                       static_cast<u32x2 *>(q), static_cast<uint8_t *>(e8m0), nchunks, full);
+  else
+    hipLaunchKernelGGL((mx8_kernel<U, T, 4, FP8Q_XCD_CHUNK>), dim3(grid_for_tiles((full + T - 1) / T, 4)),
+                       dim3(256), 0, stream, static_cast<const u32x4 *>(w),
+                       static_cast<u32x2 *>(q), static_cast<uint8_t *>(e8m0), nchunks, full);
   return hipGetLastError();
 }
 

@@ -139,6 +139,17 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #ifndef FP8Q_QUANT_WIDE_XCD
 #define FP8Q_QUANT_WIDE_XCD 256
 #endif
+// Below FP8Q_QUANT_WIDE_N: workgroups of FP8Q_QUANT_MID_W waves in XCD runs
+// of FP8Q_QUANT_MID_C.  Re-measured at 16-256 MiB with the kernels' current
+// store waits and occupancy caps: 2-, 8- and 16-wave workgroups (XCD runs of
+// the same bytes, capped and uncapped) were 1.5-4.5% slower than 4 at 64 MiB
+// and no faster elsewhere.
+#ifndef FP8Q_QUANT_MID_W
+#define FP8Q_QUANT_MID_W 4
+#endif
+#ifndef FP8Q_QUANT_MID_C
+#define FP8Q_QUANT_MID_C FP8Q_XCD_CHUNK
+#endif
 
 // One-wave workgroups wait for their code stores to be acknowledged before
 // their scales leave (s_waitcnt vmcnt(0) at the top of each round's flush),
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
                                                           uint64_t full_tiles) {
   constexpr uint64_t kChunks = U * kWave;          // 16-byte chunks per tile
   constexpr uint32_t kTileBlocks = 4 * U;
-  __shared__ float wg_scales[W * T * kTileBlocks + (W == 4 ? FP8Q_QUANT_LDS_PAD_W4 / 4
+  __shared__ float wg_scales[W * T * kTileBlocks + (W != 1 ? FP8Q_QUANT_LDS_PAD_W4 / 4
                                                             : FP8Q_QUANT_LDS_PAD_W1 / 4)];
   const uint32_t lane = lane_id();
   workgroup_rounds<T, W, C>(
@@ -281,7 +292,7 @@ hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream
   if (n >= FP8Q_QUANT_WIDE_N)
     launch_shape<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream);
   else
-    launch_shape<FMT, 4, FP8Q_XCD_CHUNK>(x, n, q, scales, full, stream);
+    launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream);
   return hipGetLastError();
 }
 

@@ -316,6 +316,17 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
 #define FP8Q_RED8_C 16
 #endif
 
+// Below FP8Q_RED_T1_BELOW_N elements each wave takes one tile, not T: the
+// grid has twice the waves and each wave's serial chain (loads, sums,
+// stores) is half as long, which is what a small launch's time is made of.
+// Measured on MI355X (k = 8, alternated in one run): into fp32 3.35 against
+// 3.94 us at a 1 MiB payload and 6.2 against 6.5-6.7 us at 4 MiB; into bf16
+// 3.06 against 3.58 us at 1 MiB.  From 24 MiB up one tile per wave was 1.5-
+// 3.5% slower, and at 16 MiB the two were within the noise of the runs.
+#ifndef FP8Q_RED_T1_BELOW_N
+#define FP8Q_RED_T1_BELOW_N (1ull << 22)
+#endif
+
 // Dynamic LDS the single-shard dequantize into bf16 reserves per workgroup
 // (the kernel uses none), so that at most 6 of its 4-wave workgroups share a
 // CU: 437.5M elements took 206.5-207.8 us capped against 212.7-213.9 us
@@ -337,9 +348,14 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
   const uint64_t tile = (uint64_t)U * 256;
   const uint64_t full = n / tile;
   constexpr int W = reduce_waves<K, BF16>();
-  hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>),
-                     dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W),
-                     (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0, stream, P, y, n, full);
+  constexpr uint32_t lds = (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0;
+  if (n < FP8Q_RED_T1_BELOW_N)
+    hipLaunchKernelGGL((reduce_kernel<FMT, K, U, 1, BF16>), dim3(grid_for_tiles(full, W)),
+                       dim3(64 * W), lds, stream, P, y, n, full);
+  else
+    hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>),
+                       dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), lds, stream, P,
+                       y, n, full);
   return hipGetLastError();
 }
 

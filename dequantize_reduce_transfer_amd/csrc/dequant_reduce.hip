@@ -119,9 +119,13 @@ constexpr int reduce_t() {
 #ifndef FP8Q_RED_WAVES_BF16
 #define FP8Q_RED_WAVES_BF16 1            // k-peer reduce into bf16: waves per workgroup
 #endif
+#ifndef FP8Q_DEQ_WAVES
+#define FP8Q_DEQ_WAVES 4                 // single-shard dequantize: waves per workgroup
+#endif
 template <int K, bool BF16 = false>
 constexpr int reduce_waves() {
-  return (BF16 && K > 1 && K <= 8) ? FP8Q_RED_WAVES_BF16 : (K == 1 ? 4 : FP8Q_RED_WAVES);
+  return (BF16 && K > 1 && K <= 8) ? FP8Q_RED_WAVES_BF16
+                                   : (K == 1 ? FP8Q_DEQ_WAVES : FP8Q_RED_WAVES);
 }
 template <int K, bool BF16 = false>
 constexpr int reduce_xcd_chunk() {

@@ -48,3 +48,24 @@ def test_short_run_prints_one_contract_line():
     assert cb["os_cpu_count"] >= cb["affinity_cpus"] >= 1 and "cpu_model" in cb
     assert {p["point"].split()[0] for p in d["gates"]["points"]} >= {
         "quantize_e4m3", "dequant_reduce_k8_f32", "mx8_layer"}
+
+
+@pytest.mark.gpu
+def test_mid_size_only_prints_every_gated_dispatch():
+    """bench.py --mid-size-only (the profiling run of the gated mid-size
+    dispatches) prints one JSON line with a timing for each of them."""
+    from gpu_util import require_gpu
+    require_gpu()
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--mid-size-only",
+                        "--steps", "3", "--copy-reference-gib", "0"],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["mid_size_only"] is True and d["steps"] == 3
+    assert set(d["ops"]) == {"quantize_e5m2_64MiB", "quantize_e4m3_64MiB", "reduce_k8_f32_64MiB",
+                             "stress_reduce_k8_bf16_e4m3", "stress_reduce_k8_bf16_e5m2",
+                             "reduce_k16_bf16_218.75M"}
+    for rec in d["ops"].values():
+        assert 0 < rec["us_min"] <= rec["us_median"] and 0 < rec["frac_peak"] < 1

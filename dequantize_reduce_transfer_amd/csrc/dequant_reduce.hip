@@ -418,10 +418,12 @@ __device__ __forceinline__ F32Scale f32_block_scale(uint32_t amax_bits) {
 }
 
 // SCALED = false may only be used where b.f == 1 (it skips x' = v * f).
+// The quotient goes to cvt4 with no clamp: |RN(v / s)| <= quotient_bound
+// for every v of a finite block (fp8q_device.h).
 template <int FMT, bool SCALED = true>
 __device__ __forceinline__ float f32_quot(float v, const F32Scale &b) {
   const float xp = SCALED ? v * b.f : v;
-  return sat_clamp<FMT>(markstein_quotient(xp, b.sp, b.rp));
+  return markstein_quotient(xp, b.sp, b.rp);
 }
 
 // Elements [start, n) (start is block-aligned): one block per pass, two

@@ -18,6 +18,7 @@
 #define FP8Q_NT_STORE 1
 #endif
 
+
 namespace fp8q {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -109,12 +110,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Pack four fp32 values into four FP8 codes (byte i <- value i).
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  uint32_t r;
+  // The first conversion writes the low half and the second the high half,
+  // so the word they start from is never seen: it is a's own register,
+  // which saves zeroing one.
+  uint32_t r = __float_as_uint(a);
   if constexpr (FMT == 0) {
-    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)r, false);
     r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
   } else {
-    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)r, false);
     r = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, (int)r, true);
   }
   return r;
@@ -135,7 +139,7 @@ __device__ __forceinline__ float fp8_max() {
   return FMT == 0 ? 448.0f : 57344.0f;
 }
 
-// The encode step every kernel takes before cvt4: clamp to +-FP8_MAX
+// The encode step of the MXFP8 kernels before cvt4: clamp to +-FP8_MAX
 // (v_med3_f32), so that the packed conversion only rounds and the codec's
 // saturation comes from the clamp.  An input beyond the range, +-inf
 // included, becomes the largest finite code of its sign.  Callers never pass
@@ -143,6 +147,21 @@ __device__ __forceinline__ float fp8_max() {
 template <int FMT>
 __device__ __forceinline__ float sat_clamp(float v) {
   return __builtin_amdgcn_fmed3f(v, -fp8_max<FMT>(), fp8_max<FMT>());
+}
+
+// The quotient encode of the block-scale kernels (block quantize, tensorwise,
+// requantize) needs no clamp.  With s = max(RN(amax / FP8_MAX), 2^-126) for a
+// finite amax and |x| <= amax, the quotient RN(x / s) never exceeds
+// quotient_bound = FP8_MAX * (1 + 2^-23) in magnitude (the next fp32 above
+// FP8_MAX): RN(amax / M) >= (amax / M)(1 - 2^-24) where it is normal, the
+// 2^-126 floor only makes s larger, and rounding is monotone.  This is
+// checked on the host for every finite fp32 amax (quotient_bound_exhaust),
+// and cvt4 alone equals the saturating RNE encode for every fp32 in
+// [-quotient_bound, quotient_bound] (checked on the device against the
+// oracle for all of them), so the clamp could never change a code there.
+template <int FMT>
+__host__ __device__ __forceinline__ constexpr float quotient_bound() {
+  return FMT == 0 ? 0x1.c00002p+8f : 0x1.c00002p+15f;   // 448 (1 + 2^-23), 57344 (1 + 2^-23)
 }
 
 // The block scale max(RN(amax / FP8_MAX), 2^-126) without a divide.

@@ -18,6 +18,10 @@
 // scale makes a NaN sum); the oracle reads every NaN as 0x7FC0, and NaN
 // patterns are counted apart ("bf16 nan: ... differ").
 //
+// Two more passes check the encode of the block-scale kernels, which
+// convert their quotients without the clamp: cvt4 alone against the oracle
+// for every fp32 in [-quotient_bound, quotient_bound].
+//
 // Output: one line per pass, then "values: N mismatches: M" over the
 // non-NaN patterns of all passes.  Exit status 0 only when all of those
 // agree.
@@ -61,6 +65,21 @@ __global__ __launch_bounds__(256) void encode_patterns(uint32_t first, uint32_t 
                              fp8q::sat_clamp<FMT>(__uint_as_float(b + 1u)),
                              fp8q::sat_clamp<FMT>(__uint_as_float(b + 2u)),
                              fp8q::sat_clamp<FMT>(__uint_as_float(b + 3u)));
+  }
+}
+
+// The same without the clamp: the block-scale kernels (block quantize,
+// tensorwise, requantize) convert their quotients with cvt4 alone, since a
+// quotient never exceeds quotient_bound in magnitude.  Compared on
+// [-quotient_bound, quotient_bound] only.
+template <int FMT>
+__global__ __launch_bounds__(256) void encode_patterns_unclamped(uint32_t first, uint32_t *out,
+                                                                 uint32_t words) {
+  for (uint32_t w = blockIdx.x * blockDim.x + threadIdx.x; w < words;
+       w += gridDim.x * blockDim.x) {
+    const uint32_t b = first + 4u * w;
+    out[w] = fp8q::cvt4<FMT>(__uint_as_float(b), __uint_as_float(b + 1u),
+                             __uint_as_float(b + 2u), __uint_as_float(b + 3u));
   }
 }
 
@@ -194,6 +213,41 @@ int main() {
     if (pass == 2)
       printf("bf16 nan: %llu NaN patterns, %llu differ from 0x7FC0\n",
              (unsigned long long)all.nan_compared, (unsigned long long)all.nan_differ);
+    fflush(stdout);
+    total_compared += all.compared;
+    total_bad += all.mismatches;
+  }
+  // The unclamped encode on [-B, B], B = quotient_bound (both signs; the
+  // ranges end below 0xD8000000, so first + 4w + 3 never wraps).
+  const char *unames[2] = {"e4m3 unclamped", "e5m2 unclamped"};
+  for (int fmt = 0; fmt < 2; ++fmt) {
+    const float bnd = fmt == 0 ? fp8q::quotient_bound<0>() : fp8q::quotient_bound<1>();
+    uint32_t bb;
+    memcpy(&bb, &bnd, 4);
+    const uint64_t per_chunk = 4ull * kChunkWords;
+    Tally all;
+    for (int sign = 0; sign < 2; ++sign) {
+      const uint64_t lo = sign ? 0x80000000ull : 0ull, hi = lo + bb;   // inclusive
+      for (uint64_t first = lo; first <= hi; first += per_chunk) {
+        if (fmt == 0)
+          hipLaunchKernelGGL(encode_patterns_unclamped<0>, dim3(4096), dim3(256), 0, 0,
+                             (uint32_t)first, d_out, kChunkWords);
+        else
+          hipLaunchKernelGGL(encode_patterns_unclamped<1>, dim3(4096), dim3(256), 0, 0,
+                             (uint32_t)first, d_out, kChunkWords);
+        CHECK(hipGetLastError());
+        CHECK(hipMemcpy(out.data(), d_out, out.size(), hipMemcpyDeviceToHost));
+        const uint64_t cnt = std::min<uint64_t>(per_chunk, hi - first + 1);
+        const Tally t = compare_chunk(out.data(), (uint32_t)first, (uint32_t)cnt, fmt, threads);
+        if (t.mismatches && !all.mismatches)
+          printf("  first mismatch: pattern 0x%08X got 0x%02X want 0x%02X\n", t.first_bad, t.got,
+                 t.want);
+        all.compared += t.compared;
+        all.mismatches += t.mismatches;
+      }
+    }
+    printf("%s: compared %llu fp32 patterns in [-%08X, %08X], mismatches %llu\n", unames[fmt],
+           (unsigned long long)all.compared, bb, bb, (unsigned long long)all.mismatches);
     fflush(stdout);
     total_compared += all.compared;
     total_bad += all.mismatches;

@@ -49,13 +49,15 @@ CVT_BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "cv
 
 def test_encode_step_equals_oracle_for_every_fp32():
     """The kernels' FP8 encode step -- clamp to +-FP8_MAX (sat_clamp), then
-    the gfx950 packed conversion (cvt4) -- and their fp32 -> bf16 output
-    conversion (bf16_pack2), run on the device for all 2^32 fp32 patterns,
-    each result compared on the host with the oracle (integer-exact satRNE
-    in e4m3 and e5m2; round-to-nearest-even bf16).  NaN patterns
-    (2 * (2^23 - 1)) are left out of the FP8 passes, since no kernel converts
-    a NaN to FP8, and counted apart in the bf16 pass.  About 15 s, mostly the
-    oracle on the host's threads."""
+    the gfx950 packed conversion (cvt4) -- for all 2^32 fp32 patterns, the
+    block-scale kernels' unclamped encode (cvt4 alone) for every fp32 in
+    [-M (1 + 2^-23), M (1 + 2^-23)] (the range their quotients stay in), and
+    their fp32 -> bf16 output conversion (bf16_pack2) for all 2^32 fp32
+    patterns, run on the device, each result compared on the host with the
+    oracle (integer-exact satRNE in e4m3 and e5m2; round-to-nearest-even
+    bf16).  NaN patterns (2 * (2^23 - 1)) are left out of the FP8 passes,
+    since no kernel converts a NaN to FP8, and counted apart in the bf16
+    pass.  About 25 s, mostly the oracle on the host's threads."""
     require_gpu()
     if not os.path.exists(CVT_BIN):
         pytest.skip("the device check is built by __graft_entry__.build()")
@@ -65,5 +67,12 @@ def test_encode_step_equals_oracle_for_every_fp32():
     per_pass = (1 << 32) - nans
     for name in ("e4m3", "e5m2", "bf16"):
         assert "%s: compared %d fp32 patterns" % (name, per_pass) in r.stdout, r.stdout
-    assert "values: %d mismatches: 0" % (3 * per_pass) in r.stdout, r.stdout
+    # the unclamped encode of the block-scale kernels on [-B, B], B = M (1 + 2^-23)
+    unclamped = 0
+    for name, bound in (("e4m3", 0x43E00001), ("e5m2", 0x47600001)):
+        cnt = 2 * (bound + 1)
+        assert ("%s unclamped: compared %d fp32 patterns in [-%08X, %08X], mismatches 0"
+                % (name, cnt, bound, bound)) in r.stdout, r.stdout
+        unclamped += cnt
+    assert "values: %d mismatches: 0" % (3 * per_pass + unclamped) in r.stdout, r.stdout
     assert "bf16 nan: %d NaN patterns" % nans in r.stdout, r.stdout

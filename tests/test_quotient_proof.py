@@ -62,3 +62,19 @@ def test_divide_free_block_scale_exhaustive(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "mismatches: 0" in r.stdout
+
+
+def test_quotient_never_exceeds_the_unclamped_encode_range(tmp_path):
+    """The block-scale kernels convert RN(x / s) with no clamp.  For every
+    finite non-negative fp32 amax and s = max(RN(amax / M), 2^-126), the
+    largest quotient of the block, RN(amax / s), is at most M (1 + 2^-23)
+    (the next fp32 above M), for M = 448 and 57344; it reaches that value
+    for some amax, so the device check of the unclamped conversion has to
+    cover it (tests/test_gpu_helpers.py)."""
+    exe = _build(tmp_path, "quotient_bound_exhaust.c", "quotient_bound_exhaust",
+                 extra=("-fopenmp",))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "e4m3: amax values 2139095040, bound 43e00001, over: 0" in r.stdout
+    assert "e5m2: amax values 2139095040, bound 47600001, over: 0" in r.stdout
+    assert "over: 0\n" in r.stdout

@@ -198,13 +198,6 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #define FP8Q_QUANT_FLUSH_WAIT_W4 0
 #endif
 
-#ifndef FP8Q_QUANT_MID_IND
-#define FP8Q_QUANT_MID_IND 0
-#endif
-#ifndef FP8Q_QUANT_FLUSH_WAIT_IND
-#define FP8Q_QUANT_FLUSH_WAIT_IND 1
-#endif
-
 // LDS each 4-wave workgroup reserves beyond its scale staging, so that at
 // most 7 of them share a CU (160 KiB of LDS per CU: 7 x 21 KiB fits, 8 do
 // not), 28 waves instead of 32.  At a 64 MiB payload (two rounds of resident
@@ -282,13 +275,8 @@ __device__ __forceinline__ void quantize_wave_tiles(const u32x4 *__restrict__ x,
 // whole workgroup.  Storing each tile's 16U bytes from its own wave, as
 // partial lines, measured 2-8% slower at 16 MiB - 1 GiB payloads (with
 // 4-wave workgroups).  W waves per workgroup, XCD runs of C workgroups.
-//
-// IND (independent waves): each wave of the workgroup works as if it were a
-// one-wave workgroup at position p * W + w -- it takes its own T tiles per
-// round, stages their 4UT scales in its own part of the LDS array and
-// writes them itself (4UT floats, contiguous), so no wave ever waits at a
-// workgroup barrier for another; the workgroup only shares the dispatch.
-template <int FMT, int U, int T, int W, int C, bool IND>
+
+template <int FMT, int U, int T, int W, int C>
 __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restrict__ x,
                                                           u32x2 *__restrict__ q,
                                                           float *__restrict__ scales, uint64_t n,
@@ -298,49 +286,28 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
   __shared__ float wg_scales[W * T * kTileBlocks + (W != 1 ? FP8Q_QUANT_LDS_PAD_W4 / 4
                                                             : FP8Q_QUANT_LDS_PAD_W1 / 4)];
   const uint32_t lane = lane_id();
-  if constexpr (IND) {
-    const uint32_t wid = uniform(threadIdx.x / kWave);
-    float *mine = wg_scales + wid * T * kTileBlocks;
-    const uint64_t stride = (uint64_t)gridDim.x * W * T;
-    for (uint64_t t0 = ((uint64_t)block_position<C>() * W + wid) * T; t0 < full_tiles;
-         t0 += stride) {
-      quantize_wave_tiles<FMT, U, T>(x, q, mine, t0, full_tiles, lane);
-      if constexpr (FP8Q_QUANT_FLUSH_WAIT_IND != 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      // the staging writes above came from other lanes of this wave: LDS
-      // operations of one wave complete in order, and the fence keeps the
-      // compiler from moving the reads before them
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      const uint64_t left = full_tiles - t0;
-      const uint32_t cnt = (left < (uint64_t)T ? (uint32_t)left : (uint32_t)T) * kTileBlocks;
-      if (lane < cnt) scales[t0 * kTileBlocks + lane] = mine[lane];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  } else {
-    workgroup_rounds<T, W, C>(
-        full_tiles,
-        [&](uint64_t t0, uint32_t wid) {
-          quantize_wave_tiles<FMT, U, T>(x, q, wg_scales + wid * T * kTileBlocks, t0, full_tiles,
-                                         lane);
-        },
-        [&](uint64_t base, uint32_t tiles) {
-          if constexpr (W == 1 ? FP8Q_QUANT_FLUSH_WAIT_W1 != 0 : FP8Q_QUANT_FLUSH_WAIT_W4 != 0)
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-          for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
-            scales[base * kTileBlocks + i] = wg_scales[i];
-        });
-  }
+  workgroup_rounds<T, W, C>(
+      full_tiles,
+      [&](uint64_t t0, uint32_t wid) {
+        quantize_wave_tiles<FMT, U, T>(x, q, wg_scales + wid * T * kTileBlocks, t0, full_tiles,
+                                       lane);
+      },
+      [&](uint64_t base, uint32_t tiles) {
+        if constexpr (W == 1 ? FP8Q_QUANT_FLUSH_WAIT_W1 != 0 : FP8Q_QUANT_FLUSH_WAIT_W4 != 0)
+          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
+          scales[base * kTileBlocks + i] = wg_scales[i];
+      });
   if (wave_index<W, C>() == wave_count<W>() - 1)
     quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
                        scales, n, full_tiles * kChunks * 8);
 }
 
-template <int FMT, int W, int C, int T = kQuantT, bool IND = false>
+template <int FMT, int W, int C, int T = kQuantT>
 void launch_shape(const void *x, uint64_t n, void *q, float *scales, uint64_t full,
                   hipStream_t stream) {
   constexpr int U = kQuantU;
-  hipLaunchKernelGGL((quantize_kernel<FMT, U, T, W, C, IND>),
+  hipLaunchKernelGGL((quantize_kernel<FMT, U, T, W, C>),
                      dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream,
                      static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, full);
 }
@@ -349,12 +316,10 @@ template <int FMT>
 hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
   const uint64_t tile_elems = (uint64_t)kQuantU * kWave * 8;
   const uint64_t full = n / tile_elems;
-  constexpr bool kMidInd = FP8Q_QUANT_MID_IND != 0;
   if (n >= FP8Q_QUANT_WIDE_N)
     launch_shape<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream);
   else if (n >= FP8Q_QUANT_T1_BELOW_N)
-    launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C, kQuantT, kMidInd>(x, n, q, scales, full,
-                                                                            stream);
+    launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream);
   else
     launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C, 1>(x, n, q, scales, full, stream);
   return hipGetLastError();

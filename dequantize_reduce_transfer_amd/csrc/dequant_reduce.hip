@@ -265,7 +265,7 @@ __device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const TileIn<K, U
 
 // Each wave takes T consecutive tiles; the next tile's loads are issued
 // before the current tile's arithmetic.
-template <int FMT, int K, int U, int T, bool BF16>
+template <int FMT, int K, int U, int T, bool BF16, bool VS = kRedVecScales<K>>
 __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
     PeerPtrs P, void *__restrict__ y, uint64_t n, uint64_t full_tiles) {
   constexpr int W = reduce_waves<K, BF16>();
@@ -275,7 +275,6 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
   const uint64_t nw = wave_count<W>();
   const uint64_t w0 = wave_index<W, C>();
 
-  constexpr bool VS = kRedVecScales<K>;
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
     TileIn<K, U, VS> cur;
     load_tile<K, U, VS>(P, t0, lane, cur);
@@ -331,6 +330,24 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
 #define FP8Q_RED_T1_BELOW_N (1ull << 22)
 #endif
 
+// From 2 to 8 peers, launches of FP8Q_RED_T1_BELOW_N up to (not including)
+// FP8Q_RED_VS_BELOW_N elements take the vector scales (each lane loads its
+// block's scale with the codes) instead of the per-wave scale loads, which
+// the compiler issues as vector loads after the next tile's codes: since
+// loads complete in order, a tile's sums then wait for the next tile's codes
+// too.  Issued with the codes, the scales cost registers (3 waves per SIMD
+// instead of 4 at 8 peers) but no longer hold a tile back; that shortens a
+// launch's fixed cost, which is what a mid-size launch is made of.  Measured
+// on MI355X (alternated in one run; graph replay over rotating windows), the
+// intercept of time against bytes fell from 3.3 to 2.8 us at 8 peers (bf16
+// out) and from 3.3 to 2.6 us (fp32 out), 2.6-2.8 to 1.7-2.1 us at 2 and 4
+// peers; 16 MiB payloads ran 4.4-4.5% faster at 8 peers, 64 MiB 0.3-1.9%
+// faster (k = 2..8), 128 MiB the same, and 224 MiB 0.5-1% slower, so larger
+// launches keep the per-wave loads.
+#ifndef FP8Q_RED_VS_BELOW_N
+#define FP8Q_RED_VS_BELOW_N (1ull << 26)
+#endif
+
 // Dynamic LDS the single-shard dequantize into bf16 reserves per workgroup
 // (the kernel uses none), so that at most 6 of its 4-wave workgroups share a
 // CU: 437.5M elements took 206.5-207.8 us capped against 212.7-213.9 us
@@ -345,22 +362,32 @@ hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t 
 
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
-  if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_BF16)
+  if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_BF16) {
     return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
-  constexpr int U = reduce_u<K, BF16>();
-  constexpr int T = reduce_t<K, BF16>();
-  const uint64_t tile = (uint64_t)U * 256;
-  const uint64_t full = n / tile;
-  constexpr int W = reduce_waves<K, BF16>();
-  constexpr uint32_t lds = (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0;
-  if (n < FP8Q_RED_T1_BELOW_N)
-    hipLaunchKernelGGL((reduce_kernel<FMT, K, U, 1, BF16>), dim3(grid_for_tiles(full, W)),
-                       dim3(64 * W), lds, stream, P, y, n, full);
-  else
-    hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>),
-                       dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), lds, stream, P,
+  } else {
+    constexpr int U = reduce_u<K, BF16>();
+    constexpr int T = reduce_t<K, BF16>();
+    const uint64_t tile = (uint64_t)U * 256;
+    const uint64_t full = n / tile;
+    constexpr int W = reduce_waves<K, BF16>();
+    constexpr uint32_t lds = (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0;
+    const dim3 grid(grid_for_tiles((full + T - 1) / T, W));
+    if (n < FP8Q_RED_T1_BELOW_N) {
+      hipLaunchKernelGGL((reduce_kernel<FMT, K, U, 1, BF16>), dim3(grid_for_tiles(full, W)),
+                         dim3(64 * W), lds, stream, P, y, n, full);
+      return hipGetLastError();
+    }
+    if constexpr (K >= 2 && K <= 8) {
+      if (n < FP8Q_RED_VS_BELOW_N) {
+        hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16, true>), grid, dim3(64 * W), lds,
+                           stream, P, y, n, full);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16>), grid, dim3(64 * W), lds, stream, P,
                        y, n, full);
-  return hipGetLastError();
+    return hipGetLastError();
+  }
 }
 
 template <int FMT, bool BF16, int K = 1>

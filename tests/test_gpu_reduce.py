@@ -257,3 +257,33 @@ def test_scales_at_odd_word_offsets(k):
     q_o, s_o = oracle.reduce_requantize(qh, sh, fq.E4M3, fq.E5M2)
     assert_bytes_equal(host(q_r), q_o, "requantize codes")
     assert_bytes_equal(f32_bits(host(s_r)), f32_bits(s_o), "requantize scales")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("k", list(range(2, 9)))
+def test_mid_size_every_peer_count(fmt, k):
+    """2..8 peers between 2^22 and 2^26 elements take the vector-scale
+    loads (each lane fetches its block's scale with the codes): a ragged
+    size there, every output against the oracle, fp32 and bf16."""
+    dev = require_gpu()
+    n = (1 << 22) + 128 * 777 + 45
+    shards = [workloads.random_wire_shard(n, seed=5000 + 10 * k + p, fmt=fmt) for p in range(k)]
+    qs = [a.numpy() for a, _ in shards]
+    ss = [b.numpy() for _, b in shards]
+    _check_reduce(qs, ss, fmt, dev, "mid-size k=%d" % k)
+
+
+@pytest.mark.parametrize("n", [(1 << 22) - 1, 1 << 22, (1 << 26) - 1, 1 << 26])
+def test_reduce_shape_switch_sizes(n):
+    """The launch shape changes at 2^22 elements (two tiles per wave) and at
+    2^26 (vector-scale loads end): one element either side of each, k = 8,
+    fp32 out, every output's bits against the oracle."""
+    dev = require_gpu()
+    k = 8
+    shards = [workloads.random_wire_shard(n, seed=6000 + p, fmt=fq.E4M3) for p in range(k)]
+    qh = [a.numpy() for a, _ in shards]
+    sh = [b.numpy() for _, b in shards]
+    y = fq.fp8q_dequant_reduce([dev_u8(a, dev) for a in qh], [dev_f32(b, dev) for b in sh], fq.E4M3)
+    torch.cuda.synchronize()
+    assert_bytes_equal(f32_bits(host(y)), f32_bits(oracle.dequant_reduce(qh, sh, fq.E4M3)),
+                       "n=%d" % n)

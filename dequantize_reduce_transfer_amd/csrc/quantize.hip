@@ -59,14 +59,15 @@ struct BlockScale {
   bool finite;
 };
 
-// TINY: whether the block may be tiny (amax < 2^-60) and so needs f; with
-// TINY false, f is the constant 1 and the multiplies by it fold away.
-template <int FMT, bool TINY = true>
+// NOT_TINY: the caller knows amax >= 2^-60, so f is the constant 1 and the
+// multiplies by it fold away; FINITE: the caller knows the block is finite,
+// so the selects on finite fold away too.
+template <int FMT, bool NOT_TINY = false, bool FINITE = false>
 __device__ __forceinline__ BlockScale block_scale(uint32_t amax_bits) {
   BlockScale b;
-  b.finite = amax_bits < 0x7F80u;
+  b.finite = FINITE || amax_bits < 0x7F80u;
   const float s = scale_from_amax<FMT>(__uint_as_float(amax_bits << 16));  // = IEEE amax / M
-  b.f = (TINY && amax_bits < 0x2180u) ? 0x1p64f : 1.0f;      // amax < 2^-60
+  b.f = (!NOT_TINY && amax_bits < 0x2180u) ? 0x1p64f : 1.0f;  // amax < 2^-60
   b.sp = s * b.f;
   b.rp = recip_rn(b.sp);                           // = IEEE 1 / sp
   b.s = b.finite ? s : __uint_as_float(0x7FC00000u);
@@ -96,16 +97,17 @@ __device__ __forceinline__ u32x2 quant8(u32x4 v, const BlockScale &b) {
 
 // One 16-byte chunk per lane (8 elements of the block its 16-lane row
 // shares): the codes, and the block's stored scale in *s.  A chunk whose
-// wave holds no tiny block (the usual case) takes the f = 1 path, which
-// saves a multiply per element and one per block; on MI355X (together with
-// the clamp-free encode and the unzeroed conversion word, alternated in one
-// run) the 64 MiB quantize went from 71.0% to 72.3% of 8 TB/s and 512 MiB
-// from 84.4% to 84.7%.
+// wave holds only finite blocks with amax >= 2^-60 (the usual case; one
+// unsigned compare tests both) takes the NORMAL path, which saves a
+// multiply per element and the selects for non-finite blocks; on MI355X
+// (together with the clamp-free encode and the unzeroed conversion word,
+// alternated in one run) the 64 MiB quantize went from 71.0% to 72.3% of
+// 8 TB/s and 512 MiB from 84.4% to 84.7%.
 template <int FMT>
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *s) {
   const uint32_t ab = max_row16(amax_bits8(v));
-  if (!wave_any(ab < 0x2180u)) {
-    const BlockScale b = block_scale<FMT, false>(ab);
+  if (!wave_any(ab - 0x2180u >= 0x7F80u - 0x2180u)) {
+    const BlockScale b = block_scale<FMT, true, true>(ab);
     *s = b.s;
     return quant8<FMT>(v, b);
   }
@@ -157,9 +159,12 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 // 3.5e9-element gradient against 81.3-81.8% for 4 waves, 83.3-83.5% against
 // 82.4-82.6% at 512 MiB and 81.2-81.4% against 80.6-80.7% at 256 MiB, but
 // 68.6-69.5% against 70.2-70.4% at 64 MiB (there the 4x larger grid seems to
-// cost more than the barrier waits it saves).
+// cost more than the barrier waits it saves).  With the kernels' current
+// arithmetic the two shapes tie at 80-96 MiB payloads, and one-wave
+// workgroups are 0.5-0.8 points faster from 112 MiB to 224 MiB and 2.1
+// points slower at 64 MiB, so the switch sits at a 96 MiB payload.
 #ifndef FP8Q_QUANT_WIDE_N
-#define FP8Q_QUANT_WIDE_N (1ull << 27)
+#define FP8Q_QUANT_WIDE_N (3ull << 24)
 #endif
 #ifndef FP8Q_QUANT_WIDE_XCD
 #define FP8Q_QUANT_WIDE_XCD 256

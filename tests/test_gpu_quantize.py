@@ -139,3 +139,23 @@ def test_scale_outputs_at_odd_word_offsets(fmt):
         assert_bytes_equal(host(q), q_o, "codes")
         assert_bytes_equal(f32_bits(b[off:off + nb]), f32_bits(s_o), "scales")
         assert np.all(b[:off] == -2.5) and np.all(b[off + nb:] == -2.5)
+
+
+@pytest.mark.parametrize("n", [(1 << 21) - 1, 1 << 21, (3 << 24) - 1, (3 << 24) + 77])
+def test_shape_switch_sizes(n):
+    """The launch shape changes at 2^21 elements (two tiles per wave) and at
+    3 * 2^24 (one-wave workgroups): one element either side of each (the
+    last one ragged), e5m2, every code and scale against the oracle.  A
+    gradient with planted blocks near both ends -- bf16 subnormals (amax
+    below 2^-60), an inf, a NaN, zeros -- so that waves take both the
+    finite-and-normal path and the general one."""
+    dev = require_gpu()
+    x = workloads.segmented_gradient(n, seed=n % 101, device=dev, segment=1 << 20)
+    bits = workloads.bits(x).copy()
+    for base in (0, (n // 128 - 40) * 128):
+        bits[base + 128 * 3:base + 128 * 4] = np.arange(128, dtype=np.uint16) % 7 | 0x8000 * (
+            np.arange(128) % 2).astype(np.uint16)
+        bits[base + 128 * 5 + 17] = 0x7F80
+        bits[base + 128 * 7:base + 128 * 8] = 0
+        bits[base + 128 * 9 + 100] = 0xFFC1
+    _check_quantize(bits, fq.E5M2, dev, "n=%d" % n)

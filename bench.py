@@ -425,10 +425,15 @@ def median_ms(torch, fns):
     return v[len(v) // 2]
 
 
-def graph_ms(torch, fns, replays=5):
+def graph_ms(torch, fns, replays=5, runs=3, all_runs=None):
     """Per-launch device time of back-to-back launches: the launches are
     captured once into a HIP graph (torch.cuda.CUDAGraph) and the graph is
-    replayed, so host-side enqueue time never shows up between kernels."""
+    replayed, so host-side enqueue time never shows up between kernels.
+    The graph is timed `runs` times (`replays` replays each, one event pair
+    per run) and the median run is returned; the first run after a pause
+    of the device measured up to 2% slower than the rest, and one run alone
+    would carry that.  Every run's per-launch time goes to `all_runs` when a
+    list is given."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -441,16 +446,20 @@ def graph_ms(torch, fns, replays=5):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(replays):
-        g.replay()
-    b.record()
-    b.synchronize()
-    ms = a.elapsed_time(b) / (replays * len(fns))
+    per = []
+    for _ in range(runs):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        b.synchronize()
+        per.append(a.elapsed_time(b) / (replays * len(fns)))
     del g
-    return ms
+    if all_runs is not None:
+        all_runs.extend(per)
+    return sorted(per)[len(per) // 2]
 
 
 def host_latency_us(torch, fn, reps=50):
@@ -500,15 +509,18 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
             yo = (i * n) % ((1 << 28) - n) // 4 * 4
             return lambda: fq.fp8q_dequant_reduce(qs, ss, fq.E5M2, out=y[yo:yo + n])
 
-        qm = graph_ms(torch, [quant(i) for i in range(reps)])
-        rm = graph_ms(torch, [red(i) for i in range(reps)])
+        q_runs, r_runs = [], []
+        qm = graph_ms(torch, [quant(i) for i in range(reps)], all_runs=q_runs)
+        rm = graph_ms(torch, [red(i) for i in range(reps)], all_runs=r_runs)
         row = {"payload_bytes": nbytes, "elements": n,
                "quantize_us": round(qm * 1e3, 2),
                "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
                "quantize_bf16_equiv_GBps": round(2 * n / qm / 1e6, 1),
                "reduce_k8_us": round(rm * 1e3, 2),
                "reduce_k8_hbm_GBps": round(reduce_bytes_per_elem(8, 4) * n / rm / 1e6, 1),
-               "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1)}
+               "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1),
+               "quantize_us_runs": [round(v * 1e3, 2) for v in q_runs],
+               "reduce_k8_us_runs": [round(v * 1e3, 2) for v in r_runs]}
         if nbytes <= 4 << 20:
             row["quantize_host_latency_us"] = host_latency_us(torch, quant(0))
             row["reduce_k8_host_latency_us"] = host_latency_us(torch, red(0))
@@ -677,14 +689,16 @@ def stress_reduce(torch, fq, workloads, dev, reps=21):
             shards, y = sets[i % copies]
             return lambda: fq.fp8q_dequant_reduce([a for a, _ in shards], [b for _, b in shards],
                                                   fmt, out_dtype=torch.bfloat16, out=y)
+        f_runs = []
         sm = graph_ms(torch, [share(i) for i in range(reps)])
-        fm = graph_ms(torch, [full(i) for i in range(reps)])
+        fm = graph_ms(torch, [full(i) for i in range(reps)], all_runs=f_runs)
         alg = reduce_bytes_per_elem(8, 2)
         res[name] = {"share_elements": cn, "share_us": round(sm * 1e3, 2),
                      "share_hbm_GBps": round(alg * cn / sm / 1e6, 1),
                      "full_elements": n, "full_us": round(fm * 1e3, 2),
                      "full_hbm_GBps": round(alg * n / fm / 1e6, 1),
-                     "full_frac_peak": round(alg * n / fm / 1e6 / HBM_PEAK_GBS, 4)}
+                     "full_frac_peak": round(alg * n / fm / 1e6 / HBM_PEAK_GBS, 4),
+                     "full_us_runs": [round(v * 1e3, 2) for v in f_runs]}
         del sets
     return res
 

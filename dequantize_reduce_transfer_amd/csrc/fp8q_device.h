@@ -134,6 +134,17 @@ __device__ __forceinline__ f32x2 dec2(uint32_t w) {
     return __builtin_amdgcn_cvt_pk_f32_bf8((int)w, HI);
 }
 
+// E4M3 codes 0,1 (HI = false) or 2,3 (HI = true) of a dword, each times the
+// E8M0 scale 2^(e8m0 - 127), in one gfx950 scaled conversion.  The scale
+// operand's exponent field carries the E8M0 code (e8m0 << 23): code 0 scales
+// by 2^-127 and 0xFF gives NaN, as E8M0 defines.  Equal to
+// fl32(dec(q) * 2^(e8m0 - 127)) for every code and every scale, NaN as NaN
+// (checked on the device against the oracle's MXFP8 dequantize).
+template <bool HI>
+__device__ __forceinline__ f32x2 mx_dec2(uint32_t w, uint32_t e8m0) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w, __uint_as_float(e8m0 << 23), HI);
+}
+
 template <int FMT>
 __device__ __forceinline__ float fp8_max() {
   return FMT == 0 ? 448.0f : 57344.0f;

@@ -20,7 +20,10 @@
 //
 // Two more passes check the encode of the block-scale kernels, which
 // convert their quotients without the clamp: cvt4 alone against the oracle
-// for every fp32 in [-quotient_bound, quotient_bound].
+// for every fp32 in [-quotient_bound, quotient_bound].  A last pass checks
+// the MXFP8 receiver's scaled decode (mx_dec2) for every E4M3 code and every
+// E8M0 scale against the oracle's MXFP8 dequantize; NaN results are compared
+// as NaN.
 //
 // Output: one line per pass, then "values: N mismatches: M" over the
 // non-NaN patterns of all passes.  Exit status 0 only when all of those
@@ -38,6 +41,8 @@
 
 extern "C" uint8_t oracle_fp8_encode(double y, int fmt);
 extern "C" uint16_t oracle_f32_to_bf16(float f);
+extern "C" int oracle_mx8_dequantize(const uint8_t *q, const uint8_t *e8m0, size_t rows, size_t K,
+                                     void *y, int out_bf16);
 
 #define CHECK(x)                                                                      \
   do {                                                                                \
@@ -81,6 +86,20 @@ __global__ __launch_bounds__(256) void encode_patterns_unclamped(uint32_t first,
     out[w] = fp8q::cvt4<FMT>(__uint_as_float(b), __uint_as_float(b + 1u),
                              __uint_as_float(b + 2u), __uint_as_float(b + 3u));
   }
+}
+
+// The MXFP8 receiver's scaled decode (mx_dec2): for pair t = 256 c + b, the
+// E4M3 code b in all four bytes of a dword and the E8M0 scale code c, both
+// halves of the packed conversion (4 values per pair).
+__global__ __launch_bounds__(256) void mx_dec_pairs(uint32_t *out) {
+  const uint32_t t = blockIdx.x * 256 + threadIdx.x;         // 256 x 256 launch: t < 65536
+  const uint32_t b = t & 255u, c = t >> 8;
+  const uint32_t w = b * 0x01010101u;
+  const fp8q::f32x2 lo = fp8q::mx_dec2<false>(w, c), hi = fp8q::mx_dec2<true>(w, c);
+  out[4 * t + 0] = __float_as_uint(lo[0]);
+  out[4 * t + 1] = __float_as_uint(lo[1]);
+  out[4 * t + 2] = __float_as_uint(hi[0]);
+  out[4 * t + 3] = __float_as_uint(hi[1]);
 }
 
 // Word w of the chunk holds the bf16 of patterns first + 2w (low half) and
@@ -251,6 +270,44 @@ int main() {
     fflush(stdout);
     total_compared += all.compared;
     total_bad += all.mismatches;
+  }
+  // The MXFP8 scaled decode against the oracle's MXFP8 dequantize of a
+  // [256, 256] matrix whose row c holds every code b and has all its E8M0
+  // scales equal to c.
+  {
+    hipLaunchKernelGGL(mx_dec_pairs, dim3(256), dim3(256), 0, 0, d_out);
+    CHECK(hipGetLastError());
+    std::vector<uint32_t> got(4 * 65536);
+    CHECK(hipMemcpy(got.data(), d_out, got.size() * 4, hipMemcpyDeviceToHost));
+    std::vector<uint8_t> q(65536), e(256 * 8);
+    for (uint32_t i = 0; i < 65536; ++i) q[i] = (uint8_t)(i & 255u);
+    for (uint32_t i = 0; i < 256 * 8; ++i) e[i] = (uint8_t)(i / 8);
+    std::vector<float> want(65536);
+    if (oracle_mx8_dequantize(q.data(), e.data(), 256, 256, want.data(), 0) != 0) return 2;
+    uint64_t cmp = 0, bad = 0, nan = 0;
+    for (uint32_t t = 0; t < 65536; ++t) {
+      uint32_t wb;
+      memcpy(&wb, &want[t], 4);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t g = got[4 * t + j];
+        ++cmp;
+        if (is_nan_pattern(wb) || is_nan_pattern(g)) {
+          ++nan;
+          if (is_nan_pattern(wb) != is_nan_pattern(g)) ++bad;
+        } else if (g != wb) {
+          if (!bad)
+            printf("  first mismatch: code 0x%02X scale %u got 0x%08X want 0x%08X\n", t & 255u,
+                   t >> 8, g, wb);
+          ++bad;
+        }
+      }
+    }
+    printf("mx scaled decode: compared %llu values (every code x every E8M0 scale, 4 positions), "
+           "NaN %llu, mismatches %llu\n", (unsigned long long)cmp, (unsigned long long)nan,
+           (unsigned long long)bad);
+    fflush(stdout);
+    total_compared += cmp;
+    total_bad += bad;
   }
   CHECK(hipFree(d_out));
   printf("values: %llu mismatches: %llu\n", (unsigned long long)total_compared,

@@ -51,11 +51,12 @@ def test_encode_step_equals_oracle_for_every_fp32():
     """The kernels' FP8 encode step -- clamp to +-FP8_MAX (sat_clamp), then
     the gfx950 packed conversion (cvt4) -- for all 2^32 fp32 patterns, the
     block-scale kernels' unclamped encode (cvt4 alone) for every fp32 in
-    [-M (1 + 2^-23), M (1 + 2^-23)] (the range their quotients stay in), and
+    [-M (1 + 2^-23), M (1 + 2^-23)] (the range their quotients stay in),
     their fp32 -> bf16 output conversion (bf16_pack2) for all 2^32 fp32
-    patterns, run on the device, each result compared on the host with the
-    oracle (integer-exact satRNE in e4m3 and e5m2; round-to-nearest-even
-    bf16).  NaN patterns (2 * (2^23 - 1)) are left out of the FP8 passes,
+    patterns, and the MXFP8 receiver's scaled decode (mx_dec2) for every
+    E4M3 code and E8M0 scale, run on the device, each result compared on the
+    host with the oracle (integer-exact satRNE in e4m3 and e5m2;
+    round-to-nearest-even bf16; the oracle's MXFP8 dequantize).  NaN patterns (2 * (2^23 - 1)) are left out of the FP8 passes,
     since no kernel converts a NaN to FP8, and counted apart in the bf16
     pass.  About 25 s, mostly the oracle on the host's threads."""
     require_gpu()
@@ -74,5 +75,8 @@ def test_encode_step_equals_oracle_for_every_fp32():
         assert ("%s unclamped: compared %d fp32 patterns in [-%08X, %08X], mismatches 0"
                 % (name, cnt, bound, bound)) in r.stdout, r.stdout
         unclamped += cnt
-    assert "values: %d mismatches: 0" % (3 * per_pass + unclamped) in r.stdout, r.stdout
+    # the MXFP8 receiver's scaled decode: every code x every E8M0 scale, 4 positions
+    assert "mx scaled decode: compared 262144 values" in r.stdout, r.stdout
+    assert "NaN 3064, mismatches 0" in r.stdout, r.stdout
+    assert "values: %d mismatches: 0" % (3 * per_pass + unclamped + 262144) in r.stdout, r.stdout
     assert "bf16 nan: %d NaN patterns" % nans in r.stdout, r.stdout

@@ -35,7 +35,8 @@
 // hardware packed FP8 conversion (round to nearest even): |q1| is at most
 // one fp32 ulp above FP8_MAX, and on that whole range the conversion equals
 // the saturating encode (quotient_bound in fp8q_device.h), so no clamp is
-// needed.  Blocks whose wave holds no amax below 2^-60 skip the factor f.
+// needed.  A chunk whose wave holds only finite blocks with amax >= 2^-60
+// skips the factor f and the non-finite selects (quant_chunk).
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -98,8 +99,9 @@ __device__ __forceinline__ u32x2 quant8(u32x4 v, const BlockScale &b) {
 // One 16-byte chunk per lane (8 elements of the block its 16-lane row
 // shares): the codes, and the block's stored scale in *s.  A chunk whose
 // wave holds only finite blocks with amax >= 2^-60 (the usual case; one
-// unsigned compare tests both) takes the NORMAL path, which saves a
-// multiply per element and the selects for non-finite blocks; on MI355X
+// unsigned compare tests both) takes the path where f is the constant 1 and
+// every block is finite, which saves a multiply per element and the
+// selects for non-finite blocks; on MI355X
 // (together with the clamp-free encode and the unzeroed conversion word,
 // alternated in one run) the 64 MiB quantize went from 71.0% to 72.3% of
 // 8 TB/s and 512 MiB from 84.4% to 84.7%.

@@ -148,6 +148,55 @@ def test_quantize_and_reduce_beyond_2_pow_32_elements():
     assert_bf16_parity(host(y[et]), want, "reduce past 2^32")
 
 
+def test_requantize_beyond_2_pow_32_elements():
+    """The reduce -> requantize of one shard of n = 2^32 + 12345 elements
+    (e4m3 in, e5m2 out): blocks around element 2^32, the ragged last block
+    and random blocks against the oracle."""
+    dev = require_gpu()
+    n = (1 << 32) + 12345
+    x = workloads.segmented_gradient(n, seed=5, device=dev, segment=1 << 28)
+    q, s = fq.fp8q_quantize(x, fq.E4M3)
+    del x
+    q2, s2 = fq.fp8q_dequant_reduce_requantize([q], [s], fq.E4M3, fq.E5M2)
+    torch.cuda.synchronize()
+    nb = (n + 127) // 128
+    idx = _sample(nb - 1, 4096, seed=8, always=[(1 << 32) // 128 - 1, (1 << 32) // 128,
+                                                (1 << 32) // 128 + 1])
+    it = torch.from_numpy(idx).to(dev)
+    qb = host(q[:(nb - 1) * 128].view(-1, 128)[it]).ravel()
+    q_o, s_o = oracle.reduce_requantize([qb], [host(s[it])], fq.E4M3, fq.E5M2)
+    assert_bytes_equal(host(q2[:(nb - 1) * 128].view(-1, 128)[it]).ravel(), q_o, "codes")
+    assert_bytes_equal(f32_bits(host(s2[it])), f32_bits(s_o), "scales")
+    tq, ts = oracle.reduce_requantize([host(q[(nb - 1) * 128:])], [host(s[nb - 1:])], fq.E4M3,
+                                      fq.E5M2)
+    assert_bytes_equal(host(q2[(nb - 1) * 128:]), tq, "tail codes")
+    assert_bytes_equal(f32_bits(host(s2[nb - 1:])), f32_bits(ts), "tail scale")
+    del q, s, q2, s2
+    torch.cuda.empty_cache()
+
+
+def test_mx8_quantize_and_dequantize_beyond_2_pow_32_elements():
+    """MXFP8 of a [2^21 + 1, 2048] weight (2^32 + 2048 elements; the last row
+    starts at element 2^32) and its receiver's dequantize into bf16: rows
+    around element 2^32 and random rows against the oracle."""
+    dev = require_gpu()
+    rows, K = (1 << 21) + 1, 2048
+    w = workloads.kaiming_uniform((rows, K), seed=9, device=dev)
+    q, e = fq.mx8_quantize(w)
+    torch.cuda.synchronize()
+    idx = _sample(rows, 512, seed=10, always=[(1 << 21) - 2, (1 << 21) - 1, 1 << 21])
+    it = torch.from_numpy(idx).to(dev)
+    q_o, e_o = oracle.mx8_quantize(host(w[it]))
+    assert_bytes_equal(host(q[it]), q_o, "mx codes")
+    assert_bytes_equal(host(e[it]), e_o, "mx e8m0")
+    del w
+    y = fq.mx8_dequantize(q, e, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_bf16_parity(host(y[it]), oracle.mx8_dequantize(q_o, e_o, out_bf16=True), "mx dequantize")
+    del q, e, y
+    torch.cuda.empty_cache()
+
+
 def test_pi05_gradient_quantize_e5m2_full():
     """The same 3.5e9-element gradient quantized to e5m2 (sampled blocks)."""
     dev = require_gpu()

@@ -310,6 +310,69 @@ __global__ __launch_bounds__(64 * W) void quantize_kernel(const u32x4 *__restric
                        scales, n, full_tiles * kChunks * 8);
 }
 
+// The last FP8Q_QUANT_TAIL_TILES tiles of a launch (at least; the split is
+// rounded to an XCD run) go one per wave instead of two, so that the
+// launch's final waves carry half the serial chain and the drain at its end
+// is shorter.  On MI355X (graph replay over rotating windows, alternated in
+// one run) a tail of 4096 tiles took the 64 MiB quantize from 72.5% to 74.5%
+// of 8 TB/s, 48 MiB from 69.2% to 71.3% and 80-94 MiB up 1.4-1.5 points;
+// with one-wave workgroups 96 and 192 MiB gained 0.8-0.9 points and 256 MiB
+// to the 3.5e9-element gradient moved within 0.1%.  Tails of 1024-3072
+// tiles gained nothing and 6144 less; with one-wave workgroups 8192 tied
+// and 16384 lost up to 1.2 points.  Launches with fewer than twice the tail
+// in tiles (below 16 MiB) keep a uniform shape: at 8 MiB an all-one-tile
+// grid was 0.5 points slower.
+#ifndef FP8Q_QUANT_TAIL_TILES
+#define FP8Q_QUANT_TAIL_TILES 4096
+#endif
+
+// A launch with a one-tile tail: workgroups at positions below q2 take two
+// tiles per wave (tiles [2W p, 2W p + 2W) for position p), the rest one tile
+// per wave (from 2W q2 on).  q2 is a multiple of the XCD run C, and the XCD
+// map (block_position) keeps positions within their dispatch round, so the
+// one-tile workgroups come last in dispatch order up to one round.  The
+// grid covers every tile in one pass (its launcher checks the dispatch
+// cap); the scale flush and the ragged tail are as in quantize_kernel.
+template <int FMT, int U, int W, int C>
+__global__ __launch_bounds__(64 * W) void quantize_split_kernel(const u32x4 *__restrict__ x,
+                                                                u32x2 *__restrict__ q,
+                                                                float *__restrict__ scales,
+                                                                uint64_t n, uint64_t full_tiles,
+                                                                uint32_t q2) {
+  constexpr uint64_t kChunks = U * kWave;
+  constexpr uint32_t kTileBlocks = 4 * U;
+  __shared__ float wg_scales[W * 2 * kTileBlocks + (W != 1 ? FP8Q_QUANT_LDS_PAD_W4 / 4
+                                                            : FP8Q_QUANT_LDS_PAD_W1 / 4)];
+  const uint32_t lane = lane_id();
+  const uint32_t wid = uniform(threadIdx.x / kWave);
+  const uint32_t pos = block_position<C>();
+  uint64_t base;
+  uint32_t wg_tiles;
+  if (pos < q2) {
+    base = (uint64_t)pos * W * 2;
+    wg_tiles = W * 2;
+    const uint64_t t0 = base + (uint64_t)wid * 2;
+    if (t0 < full_tiles)
+      quantize_wave_tiles<FMT, U, 2>(x, q, wg_scales + wid * 2 * kTileBlocks, t0, full_tiles,
+                                     lane);
+  } else {
+    base = (uint64_t)q2 * W * 2 + (uint64_t)(pos - q2) * W;
+    wg_tiles = W;
+    const uint64_t t0 = base + wid;
+    if (t0 < full_tiles)
+      quantize_wave_tiles<FMT, U, 1>(x, q, wg_scales + wid * kTileBlocks, t0, full_tiles, lane);
+  }
+  __syncthreads();
+  if constexpr (W == 1 && FP8Q_QUANT_FLUSH_WAIT_W1 != 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const uint64_t left = base < full_tiles ? full_tiles - base : 0;
+  const uint32_t tiles = left < wg_tiles ? (uint32_t)left : wg_tiles;
+  for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
+    scales[base * kTileBlocks + i] = wg_scales[i];
+  if (wave_index<W, C>() == wave_count<W>() - 1)
+    quantize_tail<FMT>(reinterpret_cast<const uint16_t *>(x), reinterpret_cast<uint8_t *>(q),
+                       scales, n, full_tiles * kChunks * 8);
+}
+
 template <int FMT, int W, int C, int T = kQuantT>
 void launch_shape(const void *x, uint64_t n, void *q, float *scales, uint64_t full,
                   hipStream_t stream) {
@@ -319,16 +382,38 @@ void launch_shape(const void *x, uint64_t n, void *q, float *scales, uint64_t fu
                      static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, full);
 }
 
+// A launch of the split kernel: the first q2 workgroups (a multiple of the
+// XCD run C) take two tiles per wave, the rest one.  Returns false, launching
+// nothing, when its grid would pass the dispatch cap (the caller then takes
+// the grid-stride kernel).  Needs full >= FP8Q_QUANT_TAIL_TILES.
+template <int FMT, int W, int C>
+bool launch_split(const void *x, uint64_t n, void *q, float *scales, uint64_t full,
+                  hipStream_t stream) {
+  const uint64_t tail = FP8Q_QUANT_TAIL_TILES;
+  const uint64_t q2 = (full - tail) / (2 * W) / C * C;
+  const uint64_t wgs = q2 + (full - q2 * 2 * W + W - 1) / W;
+  if (wgs > kMaxWorkgroups) return false;
+  hipLaunchKernelGGL((quantize_split_kernel<FMT, kQuantU, W, C>), dim3((uint32_t)wgs),
+                     dim3(64 * W), 0, stream, static_cast<const u32x4 *>(x),
+                     static_cast<u32x2 *>(q), scales, n, full, (uint32_t)q2);
+  return true;
+}
+
 template <int FMT>
 hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream_t stream) {
   const uint64_t tile_elems = (uint64_t)kQuantU * kWave * 8;
   const uint64_t full = n / tile_elems;
-  if (n >= FP8Q_QUANT_WIDE_N)
-    launch_shape<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream);
-  else if (n >= FP8Q_QUANT_T1_BELOW_N)
-    launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream);
-  else
+  const bool split = FP8Q_QUANT_TAIL_TILES > 0 && full >= 2 * (uint64_t)FP8Q_QUANT_TAIL_TILES;
+  if (n >= FP8Q_QUANT_WIDE_N) {
+    if (!(split && launch_split<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream)))
+      launch_shape<FMT, 1, FP8Q_QUANT_WIDE_XCD>(x, n, q, scales, full, stream);
+  } else if (n >= FP8Q_QUANT_T1_BELOW_N) {
+    if (!(split &&
+          launch_split<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream)))
+      launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream);
+  } else {
     launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C, 1>(x, n, q, scales, full, stream);
+  }
   return hipGetLastError();
 }
 

@@ -141,11 +141,13 @@ def test_scale_outputs_at_odd_word_offsets(fmt):
         assert np.all(b[:off] == -2.5) and np.all(b[off + nb:] == -2.5)
 
 
-@pytest.mark.parametrize("n", [(1 << 21) - 1, 1 << 21, (3 << 24) - 1, (3 << 24) + 77])
+@pytest.mark.parametrize("n", [(1 << 21) - 1, 1 << 21, (1 << 23) - 1, (1 << 23) + 77,
+                               (3 << 24) - 1, (3 << 24) + 77])
 def test_shape_switch_sizes(n):
-    """The launch shape changes at 2^21 elements (two tiles per wave) and at
-    3 * 2^24 (one-wave workgroups): one element either side of each (the
-    last one ragged), e5m2, every code and scale against the oracle.  A
+    """The launch shape changes at 2^21 elements (two tiles per wave), at
+    2^23 (a one-tile tail of 4096 tiles) and at 3 * 2^24 (one-wave
+    workgroups): one element either side of each (ragged above), e5m2,
+    every code and scale against the oracle.  A
     gradient with planted blocks near both ends -- bf16 subnormals (amax
     below 2^-60), an inf, a NaN, zeros -- so that waves take both the
     finite-and-normal path and the general one."""

@@ -263,8 +263,28 @@ __device__ __forceinline__ void reduce_tile(const PeerPtrs &P, const TileIn<K, U
                  acc[u][3]);
 }
 
-// Each wave takes T consecutive tiles; the next tile's loads are issued
-// before the current tile's arithmetic.
+// A wave's T consecutive tiles [t0, t0 + T) (those below full_tiles), the
+// next tile's loads issued before the current tile's arithmetic.
+template <int FMT, int K, int U, int T, bool BF16, bool VS>
+__device__ __forceinline__ void reduce_wave_tiles(const PeerPtrs &P, void *__restrict__ y,
+                                                  uint64_t t0, uint64_t full_tiles,
+                                                  uint32_t lane) {
+  TileIn<K, U, VS> cur;
+  load_tile<K, U, VS>(P, t0, lane, cur);
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const uint64_t t = t0 + j;
+    if (t >= full_tiles) break;
+    TileIn<K, U, VS> nxt;
+    const bool more = (j + 1 < T) && (t + 1 < full_tiles);
+    if (more) load_tile<K, U, VS>(P, t + 1, lane, nxt);
+    reduce_tile<FMT, K, U, VS, BF16>(P, cur, y, t, lane);
+    if (more) cur = nxt;
+  }
+}
+
+// Each wave takes T consecutive tiles per pass (grid-stride past the
+// dispatch cap).
 template <int FMT, int K, int U, int T, bool BF16, bool VS = kRedVecScales<K>>
 __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
     PeerPtrs P, void *__restrict__ y, uint64_t n, uint64_t full_tiles) {
@@ -275,6 +295,8 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
   const uint64_t nw = wave_count<W>();
   const uint64_t w0 = wave_index<W, C>();
 
+  // (the loop of reduce_wave_tiles, written out: calling the helper here
+  // changed the compiled loop, and this kernel's code is the measured one)
   for (uint64_t t0 = w0 * T; t0 < full_tiles; t0 += nw * T) {
     TileIn<K, U, VS> cur;
     load_tile<K, U, VS>(P, t0, lane, cur);
@@ -288,6 +310,29 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
       reduce_tile<FMT, K, U, VS, BF16>(P, cur, y, t, lane);
       if (more) cur = nxt;
     }
+  }
+  if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
+}
+
+// One pass with a one-tile tail: waves below q2w take two tiles (tiles
+// [2w, 2w + 2) for wave w), the rest one (from 2 q2w on), so the launch's
+// last waves carry half the serial chain.  q2w is a multiple of an XCD
+// run's waves, so the one-tile waves come last in dispatch order up to one
+// round.  The grid covers every tile (its launcher checks the dispatch cap).
+template <int FMT, int K, int U, bool BF16, bool VS = kRedVecScales<K>>
+__global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_kernel(
+    PeerPtrs P, void *__restrict__ y, uint64_t n, uint64_t full_tiles, uint64_t q2w) {
+  constexpr int W = reduce_waves<K, BF16>();
+  constexpr int C = reduce_xcd_chunk<K, BF16>();
+  constexpr uint64_t kTile = (uint64_t)U * 256;
+  const uint32_t lane = lane_id();
+  const uint64_t nw = wave_count<W>();
+  const uint64_t w0 = wave_index<W, C>();
+  if (w0 < q2w) {
+    reduce_wave_tiles<FMT, K, U, 2, BF16, VS>(P, y, 2 * w0, full_tiles, lane);
+  } else {
+    const uint64_t t0 = 2 * q2w + (w0 - q2w);
+    if (t0 < full_tiles) reduce_wave_tiles<FMT, K, U, 1, BF16, VS>(P, y, t0, full_tiles, lane);
   }
   if (w0 == nw - 1) reduce_tail<FMT, K, BF16>(P, y, n, full_tiles * kTile);
 }
@@ -347,6 +392,24 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_kernel(
 #ifndef FP8Q_RED_VS_BELOW_N
 #define FP8Q_RED_VS_BELOW_N (1ull << 26)
 #endif
+// With the vector scales, from FP8Q_RED_TAIL_MIN_K peers, the last
+// FP8Q_RED_TAIL_TILES tiles of a launch go one per wave instead of two
+// (reduce_split_kernel), as in the block quantize: the launch's final waves
+// carry half the serial chain, so its drain is shorter.  On MI355X (graph
+// replay over rotating windows, alternated in one run, % of 8 TB/s), with
+// 4096 tiles: 8 peers into bf16 67.0 -> 70.7 at 16 MiB, 74.1 -> 76.9 at
+// 32 MiB, 79.4 -> 80.4 at 64 MiB; into fp32 68.9 -> 72.1 at 16 MiB and
+// 79.8 -> 80.4 at 64 MiB; 4 and 6 peers up 2.2-4.5 points at 16 MiB and
+// -0.3 to +1.3 at 64 MiB.  Tails of 8192 and 16384 tiles gained less.
+// With fewer peers (2, 3) or on the per-wave scale path (from 2^26
+// elements, 128 MiB: 0.5-2 points slower) it did not pay, nor for the
+// single-shard dequantize.
+#ifndef FP8Q_RED_TAIL_TILES
+#define FP8Q_RED_TAIL_TILES 4096
+#endif
+#ifndef FP8Q_RED_TAIL_MIN_K
+#define FP8Q_RED_TAIL_MIN_K 4
+#endif
 
 // Dynamic LDS the single-shard dequantize into bf16 reserves per workgroup
 // (the kernel uses none), so that at most 6 of its 4-wave workgroups share a
@@ -379,6 +442,20 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
     }
     if constexpr (K >= 2 && K <= 8) {
       if (n < FP8Q_RED_VS_BELOW_N) {
+        if constexpr (K >= FP8Q_RED_TAIL_MIN_K && T == 2) {
+          // the last FP8Q_RED_TAIL_TILES tiles one per wave (reduce_split_kernel)
+          constexpr uint64_t kTail = FP8Q_RED_TAIL_TILES;
+          constexpr uint64_t kRunWaves = (uint64_t)W * reduce_xcd_chunk<K, BF16>();
+          if (kTail > 0 && full >= 2 * kTail) {
+            const uint64_t q2w = (full - kTail) / 2 / kRunWaves * kRunWaves;
+            const uint64_t wgs = (q2w + (full - 2 * q2w) + W - 1) / W;
+            if (wgs <= kMaxWorkgroups) {
+              hipLaunchKernelGGL((reduce_split_kernel<FMT, K, U, BF16, true>), dim3((uint32_t)wgs),
+                                 dim3(64 * W), lds, stream, P, y, n, full, q2w);
+              return hipGetLastError();
+            }
+          }
+        }
         hipLaunchKernelGGL((reduce_kernel<FMT, K, U, T, BF16, true>), grid, dim3(64 * W), lds,
                            stream, P, y, n, full);
         return hipGetLastError();

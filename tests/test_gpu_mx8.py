@@ -111,3 +111,23 @@ def test_scale_pointer_at_any_byte_offset(offset):
     b = host(buf)
     assert_bytes_equal(b[offset:offset + ne], e_o.ravel(), "e8m0")
     assert np.all(b[:offset] == 0xA5) and np.all(b[offset + ne:] == 0xA5)
+
+
+@pytest.mark.parametrize("rows", [(1 << 16) - 1, 1 << 16])
+def test_shape_switch_sizes(rows):
+    """The MXFP8 launch changes shape at 2^27 elements (one-wave workgroups
+    whose last 4096 tiles go one per wave): [rows, 2048] weights either
+    side of it, sampled rows (the first, the last and random ones) against
+    the oracle."""
+    dev = require_gpu()
+    K = 2048
+    w = workloads.kaiming_uniform((rows, K), seed=rows % 13, device=dev)
+    q, e = fq.mx8_quantize(w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(rows)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(rows - 64, rows),
+                                    rng.integers(0, rows, 2048)]))
+    it = torch.from_numpy(idx).to(dev)
+    q_o, e_o = oracle.mx8_quantize(host(w[it]))
+    assert_bytes_equal(host(q[it]), q_o, "codes rows=%d" % rows)
+    assert_bytes_equal(host(e[it]), e_o, "e8m0 rows=%d" % rows)

@@ -695,6 +695,61 @@ __global__ __launch_bounds__(64 * W) void requant8_kernel(PeerPtrs P, u32x2 *__r
     requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
 }
 
+// One pass with a one-tile tail, as the block quantize's split kernel:
+// workgroups at positions below q2 (a multiple of the XCD run C) take two
+// tiles per wave, the rest one, so the launch's last waves carry half the
+// serial chain.  The scale flush and the ragged tail are as in
+// requant8_kernel.
+template <int FIN, int FOUT, int K, int U, int W, int C>
+__global__ __launch_bounds__(64 * W) void requant8_split_kernel(PeerPtrs P, u32x2 *__restrict__ qo,
+                                                                float *__restrict__ so, uint64_t n,
+                                                                uint64_t full_tiles, uint32_t q2) {
+  constexpr uint64_t kTile = (uint64_t)U * 512;
+  constexpr uint32_t kTileBlocks = 4 * U;
+  const uint32_t lane = lane_id();
+  const uint32_t wid = uniform(threadIdx.x / kWave);
+  const uint32_t pos = block_position<C>();
+  __shared__ float wg_scales[W * 2 * kTileBlocks];
+  uint64_t base;
+  uint32_t wg_tiles;
+  if (pos < q2) {
+    base = (uint64_t)pos * W * 2;
+    wg_tiles = W * 2;
+    const uint64_t t0 = base + (uint64_t)wid * 2;
+    if (t0 < full_tiles)
+      requant8_wave_tiles<FIN, FOUT, K, U, 2>(P, qo, wg_scales + wid * 2 * kTileBlocks, t0,
+                                              full_tiles, lane);
+  } else {
+    base = (uint64_t)q2 * W * 2 + (uint64_t)(pos - q2) * W;
+    wg_tiles = W;
+    const uint64_t t0 = base + wid;
+    if (t0 < full_tiles)
+      requant8_wave_tiles<FIN, FOUT, K, U, 1>(P, qo, wg_scales + wid * kTileBlocks, t0,
+                                              full_tiles, lane);
+  }
+  __syncthreads();
+  const uint64_t left = base < full_tiles ? full_tiles - base : 0;
+  const uint32_t tiles = left < wg_tiles ? (uint32_t)left : wg_tiles;
+  for (uint32_t i = threadIdx.x; i < tiles * kTileBlocks; i += 64 * W)
+    so[base * kTileBlocks + i] = wg_scales[i];
+  if (wave_index<W, C>() == wave_count<W>() - 1)
+    requant_tail<FIN, FOUT, K>(P, reinterpret_cast<uint8_t *>(qo), so, n, full_tiles * kTile);
+}
+
+// From FP8Q_RQ8_TAIL_MIN_K peers the last FP8Q_RQ8_TAIL_TILES tiles of a
+// launch go one per wave (requant8_split_kernel).  On MI355X (graph replay
+// over rotating windows, alternated in one run, e4m3 -> e4m3, % of 8 TB/s),
+// with 4096 tiles: 4 peers 55.2 -> 59.7 at 16 MiB, 75.1 -> 76.3 at 64 MiB,
+// 80.9 -> 81.6 at 128 MiB; 8 peers 61.5 -> 62.8, 77.3 -> 78.0 and equal at
+// 128 MiB.  With one peer it lost 1.8 points at 16 MiB, so fewer peers keep
+// requant8_kernel.
+#ifndef FP8Q_RQ8_TAIL_TILES
+#define FP8Q_RQ8_TAIL_TILES 4096
+#endif
+#ifndef FP8Q_RQ8_TAIL_MIN_K
+#define FP8Q_RQ8_TAIL_MIN_K 4
+#endif
+
 // Tile shape: U = 2 groups of 512 elements per tile, T = 2 tiles per wave,
 // 4-wave workgroups, at every peer count.  Against the previous requantize
 // (four codes per lane, a block across 32 lanes, its tile shape tuned per
@@ -728,6 +783,20 @@ void launch_requant8(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStre
   constexpr int T = FP8Q_RQ8_T;
   constexpr int W = 4;
   const uint64_t full = n / ((uint64_t)U * 512);
+  constexpr uint64_t kTail = FP8Q_RQ8_TAIL_TILES;
+  constexpr uint64_t C = FP8Q_XCD_CHUNK_RQ;
+  if constexpr (T == 2 && kTail > 0 && K >= FP8Q_RQ8_TAIL_MIN_K) {
+    if (full >= 2 * kTail) {
+      const uint64_t q2 = (full - kTail) / (2 * W) / C * C;
+      const uint64_t wgs = q2 + (full - q2 * 2 * W + W - 1) / W;
+      if (wgs <= kMaxWorkgroups) {
+        hipLaunchKernelGGL((requant8_split_kernel<FIN, FOUT, K, U, W, FP8Q_XCD_CHUNK_RQ>),
+                           dim3((uint32_t)wgs), dim3(64 * W), 0, stream, P,
+                           static_cast<u32x2 *>(qo), so, n, full, (uint32_t)q2);
+        return;
+      }
+    }
+  }
   hipLaunchKernelGGL((requant8_kernel<FIN, FOUT, K, U, T, W, FP8Q_XCD_CHUNK_RQ>),
                      dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P,
                      static_cast<u32x2 *>(qo), so, n, full);

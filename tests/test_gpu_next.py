@@ -264,3 +264,15 @@ def test_requantize_quotient_across_every_scale_range(fmt_out):
     q_o, s_o = oracle.reduce_requantize(qs, ss, fq.E4M3, fmt_out)
     assert_bytes_equal(host(q_g), q_o, "codes")
     assert_bytes_equal(f32_bits(host(s_g)), f32_bits(s_o), "scales")
+
+
+@pytest.mark.parametrize("k", [4, 8, 16])
+def test_requantize_one_tile_tail_sizes(k):
+    """From 4 peers and 2^23 elements the requantize ends with one-tile waves
+    (its last 4096 tiles): a ragged size past that, e5m2 -> e4m3, every code
+    and scale against the oracle."""
+    dev = require_gpu()
+    n = (1 << 23) + 1024 * 321 + 77
+    shards = [workloads.random_wire_shard(n, seed=900 + 10 * k + p, fmt=1) for p in range(k)]
+    _check_requant([a.numpy() for a, _ in shards], [b.numpy() for _, b in shards], 1, 0, dev,
+                   "tail k=%d" % k)

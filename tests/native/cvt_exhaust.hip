@@ -1,7 +1,7 @@
 // cvt_exhaust.hip -- device check of the kernels' FP8 encode step against
 // the oracle, over every fp32 bit pattern.
 //
-// Every kernel turns an fp32 value into an FP8 code the same way: clamp to
+// The MXFP8 kernels turn an fp32 value into an FP8 code by a clamp to
 // +-FP8_MAX (sat_clamp), then the gfx950 packed conversion (cvt4), four
 // values per dword.  This program runs exactly those two helpers from
 // fp8q_device.h on the GPU for all 2^32 fp32 patterns, in both formats, and

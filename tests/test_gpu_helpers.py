@@ -48,8 +48,8 @@ CVT_BIN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "cv
 
 
 def test_encode_step_equals_oracle_for_every_fp32():
-    """The kernels' FP8 encode step -- clamp to +-FP8_MAX (sat_clamp), then
-    the gfx950 packed conversion (cvt4) -- for all 2^32 fp32 patterns, the
+    """The MXFP8 kernels' FP8 encode step -- clamp to +-FP8_MAX (sat_clamp),
+    then the gfx950 packed conversion (cvt4) -- for all 2^32 fp32 patterns, the
     block-scale kernels' unclamped encode (cvt4 alone) for every fp32 in
     [-M (1 + 2^-23), M (1 + 2^-23)] (the range their quotients stay in),
     their fp32 -> bf16 output conversion (bf16_pack2) for all 2^32 fp32

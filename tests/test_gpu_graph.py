@@ -3,7 +3,6 @@ caller can capture them in a HIP graph (torch.cuda.CUDAGraph).  Replays must
 equal the eager result every time, with eager work and synchronisations in
 between (tensorwise quantize included: it reuses its scale slot as the amax
 slot, which must be reset on every replay)."""
-import numpy as np
 import pytest
 import torch
 

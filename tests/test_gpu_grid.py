@@ -1,7 +1,6 @@
 """Sizes whose grids hold several whole rounds of the XCD-aware workgroup
 map plus a remainder that keeps the identity (and a ragged tail), checked in
 full against the oracle: a wrong map would drop or repeat whole tiles."""
-import numpy as np
 import pytest
 import torch
 

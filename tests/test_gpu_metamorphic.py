@@ -1,7 +1,6 @@
 """Metamorphic properties checked on the GPU path itself (beyond parity):
 scaling the input by a power of two keeps every code and scales the scales,
 negating the input flips only sign bits, and rejected calls write nothing."""
-import numpy as np
 import pytest
 import torch
 

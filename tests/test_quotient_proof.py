@@ -9,7 +9,6 @@ formula from quantize.hip; it shares no code with the kernel or the oracle.
 import os
 import subprocess
 
-import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 

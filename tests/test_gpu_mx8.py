@@ -113,6 +113,31 @@ def test_scale_pointer_at_any_byte_offset(offset):
     assert np.all(b[:offset] == 0xA5) and np.all(b[offset + ne:] == 0xA5)
 
 
+@pytest.mark.parametrize("offset", [1, 4])
+def test_scale_pointer_at_byte_offsets_one_wave_shape(offset):
+    """The same on the one-wave shape (from 2^27 elements, ending with
+    one-tile waves): [2^16 + 3, 2048] weights, E8M0 output at byte offsets
+    1 and 4 between canaries, sampled rows (the first, the last and random
+    ones) against the oracle."""
+    dev = require_gpu()
+    rows, K = (1 << 16) + 3, 2048
+    w = workloads.kaiming_uniform((rows, K), seed=40 + offset, device=dev)
+    ne = rows * K // 32
+    buf = torch.full((ne + 8,), 0xA5, dtype=torch.uint8, device=dev)
+    q, _ = fq.mx8_quantize(w, e8m0_out=buf[offset:offset + ne])
+    torch.cuda.synchronize()
+    e = buf[offset:offset + ne].view(rows, K // 32)
+    rng = np.random.default_rng(offset)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(rows - 64, rows),
+                                    rng.integers(0, rows, 2048)]))
+    it = torch.from_numpy(idx).to(dev)
+    q_o, e_o = oracle.mx8_quantize(host(w[it]))
+    assert_bytes_equal(host(q[it]), q_o, "codes")
+    assert_bytes_equal(host(e[it]), e_o, "e8m0")
+    b = host(buf)
+    assert np.all(b[:offset] == 0xA5) and np.all(b[offset + ne:] == 0xA5)
+
+
 @pytest.mark.parametrize("rows", [(1 << 16) - 1, 1 << 16])
 def test_shape_switch_sizes(rows):
     """The MXFP8 launch changes shape at 2^27 elements (one-wave workgroups

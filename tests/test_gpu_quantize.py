@@ -141,6 +141,24 @@ def test_scale_outputs_at_odd_word_offsets(fmt):
         assert np.all(b[:off] == -2.5) and np.all(b[off + nb:] == -2.5)
 
 
+@pytest.mark.parametrize("n", [(1 << 23) + 77, (3 << 24) + 77])
+def test_scale_outputs_at_odd_word_offsets_split_shapes(n):
+    """The same on the launches that end with one-tile waves: the 4-wave
+    shape (from 2^23 elements) and the one-wave shape (from 3 * 2^24), whose
+    workgroups flush 64 and 16 scales per round."""
+    dev = require_gpu()
+    nb = (n + 127) // 128
+    x = workloads.segmented_gradient(n, seed=13, device=dev, segment=1 << 20)
+    q_o, s_o = oracle.quantize(workloads.bits(x), fq.E4M3)
+    buf = torch.full((nb + 6,), -2.5, dtype=torch.float32, device=dev)
+    q, s = fq.fp8q_quantize(x, fq.E4M3, scales_out=buf[1:1 + nb])
+    torch.cuda.synchronize()
+    b = host(buf)
+    assert_bytes_equal(host(q), q_o, "codes")
+    assert_bytes_equal(f32_bits(b[1:1 + nb]), f32_bits(s_o), "scales")
+    assert b[0] == -2.5 and np.all(b[1 + nb:] == -2.5)
+
+
 @pytest.mark.parametrize("n", [(1 << 21) - 1, 1 << 21, (1 << 23) - 1, (1 << 23) + 77,
                                (3 << 24) - 1, (3 << 24) + 77])
 def test_shape_switch_sizes(n):

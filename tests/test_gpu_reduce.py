@@ -259,6 +259,44 @@ def test_scales_at_odd_word_offsets(k):
     assert_bytes_equal(f32_bits(host(s_r)), f32_bits(s_o), "requantize scales")
 
 
+@pytest.mark.parametrize("k", [4, 8])
+def test_scales_at_odd_word_offsets_mid_size(k):
+    """The same at a mid size past 2^23 elements, where the reduce loads its
+    scales per lane and ends with one-tile waves (into fp32 and bf16) and the
+    requantize ends with one-tile waves too; the requantize's output scales
+    also start at an odd word offset, between canaries."""
+    dev = require_gpu()
+    n = (1 << 23) + 128 * 37 + 5
+    nb = (n + 127) // 128
+    shards = [workloads.random_wire_shard(n, seed=520 + p, fmt=fq.E5M2) for p in range(k)]
+    qh = [a.numpy() for a, _ in shards]
+    sh = [b.numpy() for _, b in shards]
+    qd = [dev_u8(a, dev) for a in qh]
+    sd = []
+    for p, s in enumerate(sh):
+        off = 2 * p + 3
+        buf = torch.zeros(nb + off + 3, dtype=torch.float32, device=dev)
+        buf[off:off + nb] = torch.from_numpy(s).to(dev)
+        sd.append(buf[off:off + nb])
+        assert sd[-1].data_ptr() % 8 == 4
+    want = oracle.dequant_reduce(qh, sh, fq.E5M2)
+    y = fq.fp8q_dequant_reduce(qd, sd, fq.E5M2)
+    yb = fq.fp8q_dequant_reduce(qd, sd, fq.E5M2, out_dtype=torch.bfloat16)
+    so_buf = torch.full((nb + 6,), 7.0, dtype=torch.float32, device=dev)
+    s_r = so_buf[5:5 + nb]
+    assert s_r.data_ptr() % 8 == 4
+    q_r, _ = fq.fp8q_dequant_reduce_requantize(qd, sd, fq.E5M2, fq.E4M3, scales_out=s_r)
+    torch.cuda.synchronize()
+    assert_bytes_equal(f32_bits(host(y)), f32_bits(want), "reduce fp32")
+    assert_bf16_parity(host(yb), oracle.dequant_reduce(qh, sh, fq.E5M2, out_bf16=True),
+                       "reduce bf16")
+    q_o, s_o = oracle.reduce_requantize(qh, sh, fq.E5M2, fq.E4M3)
+    assert_bytes_equal(host(q_r), q_o, "requantize codes")
+    assert_bytes_equal(f32_bits(host(s_r)), f32_bits(s_o), "requantize scales")
+    sb = host(so_buf)
+    assert np.all(sb[:5] == 7.0) and np.all(sb[5 + nb:] == 7.0), "requantize scale canaries"
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("k", list(range(2, 9)))
 def test_mid_size_every_peer_count(fmt, k):

@@ -270,9 +270,25 @@ def test_requantize_quotient_across_every_scale_range(fmt_out):
 def test_requantize_one_tile_tail_sizes(k):
     """From 4 peers and 2^23 elements the requantize ends with one-tile waves
     (its last 4096 tiles): a ragged size past that, e5m2 -> e4m3, every code
-    and scale against the oracle."""
+    and scale against the oracle.  Special blocks are planted at the start
+    and among the one-tile waves: an inf and a NaN code, peers that cancel
+    to a zero block, sums below 2^-60 (tiny scales), and sums that overflow
+    fp32 to inf (huge scales)."""
     dev = require_gpu()
     n = (1 << 23) + 1024 * 321 + 77
     shards = [workloads.random_wire_shard(n, seed=900 + 10 * k + p, fmt=1) for p in range(k)]
-    _check_requant([a.numpy() for a, _ in shards], [b.numpy() for _, b in shards], 1, 0, dev,
-                   "tail k=%d" % k)
+    qs = [a.numpy().copy() for a, _ in shards]
+    ss = [b.numpy().copy() for _, b in shards]
+    for base in (0, (n - 1024 * 1000) // 128 * 128, (n - 2048 - 77) // 128 * 128):
+        b0 = base // 128
+        qs[0][base + 5] = 0x7C                          # +inf
+        qs[1][base + 128 + 9] = 0x7F                    # NaN
+        for p in range(k):                              # block b0 + 2 cancels: +1, -1, +1, -1 ...
+            qs[p][base + 256:base + 384] = 0x3C if p % 2 == 0 else 0xBC
+            ss[p][b0 + 2] = 1.0
+        for p in range(k):                              # block b0 + 3: sums near 2^-100
+            ss[p][b0 + 3] = 2.0 ** -110
+        for p in range(k):                              # block b0 + 4: 57344 * 2^115 overflows
+            qs[p][base + 512:base + 640] = 0x7B
+            ss[p][b0 + 4] = 2.0 ** 115
+    _check_requant(qs, ss, 1, 0, dev, "tail k=%d" % k)

@@ -44,6 +44,7 @@ for _n in _log_uniform(0, 10, 2) + _log_uniform(10, 26.5, 10):
     while _n * _k > (1 << 28):
         _n //= 2
     REQUANT_CASES.append((_n, _k, int(_RNG.integers(0, 2)), int(_RNG.integers(0, 2))))
+TW_CASES = [(n, int(_RNG.integers(0, 2))) for n in _log_uniform(0, 10, 1) + _log_uniform(10, 26, 5)]
 MX_CASES = []
 for _ in range(6):
     _K = 32 * int(_RNG.integers(1, 97))
@@ -147,3 +148,16 @@ def test_mx8_random_shapes(rows, K, k, bf16):
         assert np.array_equal(np.isnan(got), np.isnan(w)), "mx receiver NaN positions"
         ok = ~np.isnan(w)
         assert_bytes_equal(f32_bits(got[ok]), f32_bits(w[ok]), "mx receiver %dx%d k=%d" % (rows, K, k))
+
+
+@pytest.mark.parametrize("n,fmt", TW_CASES, ids=["n%d-f%d" % c for c in TW_CASES])
+def test_tensorwise_random_sizes(n, fmt):
+    """The tensorwise quantize (one scale for the whole tensor) on a
+    segmented gradient whose segments span six decades of scale."""
+    dev = require_gpu()
+    bits = workloads.bits(workloads.segmented_gradient(n, seed=n % 8191, segment=1 << 16))
+    q, s = fq.fp8q_quantize_tensorwise(dev_bf16(bits, dev), fmt)
+    torch.cuda.synchronize()
+    q_o, s_o = oracle.quantize_tensorwise(bits, fmt)
+    assert_bytes_equal(host(q), q_o, "tensorwise codes n=%d" % n)
+    assert_bytes_equal(f32_bits(host(s)), f32_bits(s_o), "tensorwise scale n=%d" % n)

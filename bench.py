@@ -216,8 +216,8 @@ def cpu_baseline(smp, fmt, threads, runs=1):
     return rec, outputs
 
 
-# The GPU machine gives each GPU a share of 16 host CPUs (its worker pools are to
-# be sized to that share, whatever the machine's own count is), so the
+# A one-GPU MI355X host here gives its GPU a share of 16 CPUs (worker pools
+# are sized to that share, whatever the machine's own count is), so the
 # oracle's thread pool is capped there; the record states the machine's
 # count, the process's CPU set and the model next to the threads used.
 HOST_THREAD_CAP = 16
@@ -243,7 +243,7 @@ def host_cpus():
 
 def host_threads():
     """Host threads for the CPU baseline: the process's CPU set, at most
-    HOST_THREAD_CAP (the machine's CPU share for one GPU)."""
+    HOST_THREAD_CAP (the host's CPU share for one GPU)."""
     return max(1, min(HOST_THREAD_CAP, host_cpus()["affinity_cpus"]))
 
 
@@ -997,7 +997,7 @@ def main():
         rec, outputs = cpu_baseline(smp, fmt, threads, runs=3 if threads > 1 else 1)
         rec.update(host_cpus())
         rec["thread_cap"] = HOST_THREAD_CAP
-        rec["thread_cap_reason"] = ("the GPU box's host-CPU share for one GPU; the pool "
+        rec["thread_cap_reason"] = ("the host's CPU share for one GPU; the pool "
                                     "uses min(cap, affinity_cpus) threads")
         out["cpu_baseline"] = rec
         log("parity: the step's outputs against the oracle")

@@ -130,7 +130,8 @@ hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0, h
 
 }  // namespace fp8q
 
-// Read back by the tests (ctypes) when the library under test is this build.
+// Read back by the tests (ctypes) when the library under test is the
+// host-check build.
 extern "C" __attribute__((visibility("default"))) long fp8q_stub_calls(void) { return g_rec.calls; }
 extern "C" __attribute__((visibility("default"))) const char *fp8q_stub_last(void) {
   return g_rec.last;

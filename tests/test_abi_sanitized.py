@@ -7,7 +7,7 @@ in place of the kernels: the stubs enqueue nothing, check the invariants a
 validated call guarantees the launchers, and record each call.  Every case
 of tests/test_abi.py then runs against that build in a child process with
 the sanitizer runtime preloaded, including the accepted-call cases that only
-this build can run without a GPU.  Python's own allocator is switched to
+the host-check build can run without a GPU.  Python's own allocator is switched to
 malloc there so that a read past a short host array of peer pointers is a
 sanitizer report rather than a silent read inside a Python arena, and the
 child runs with pytest's output capture off, so that a sanitizer report that

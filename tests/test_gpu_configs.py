@@ -42,7 +42,7 @@ FMTS = [fq.E4M3, fq.E5M2]
 
 
 def _threads():
-    """The machine's CPU share for one GPU is 16; use at most that many."""
+    """The host's CPU share for one GPU is 16; use at most that many."""
     try:
         return max(1, min(16, len(os.sched_getaffinity(0))))
     except AttributeError:

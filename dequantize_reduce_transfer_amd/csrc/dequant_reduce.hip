@@ -374,6 +374,25 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 #ifndef FP8Q_RED_T1_BELOW_N
 #define FP8Q_RED_T1_BELOW_N (1ull << 22)
 #endif
+// The tile depth of those one-tile waves from FP8Q_RED_SMALL_U_FROM_N
+// elements (a 1 MiB payload) up.  Into fp32, and into bf16 from 5 peers, a
+// tile of one group (U = 1, so twice the waves again) was faster on MI355X
+// (alternated in one run, % change at 767 KiB / 1 / 2 / 4 / 7.9 MiB
+// payloads): 8 peers into fp32 +1.6 / +7.0 / +2.2 / +0.3 / +8.3, one shard
+// into fp32 -1.9 / +3.7 / +8.9 / +18.0 / +22.2, 2-7 peers into fp32 -5.5 to
+// +15.0 (gains from 2 MiB, up to 2.2% lost at 767 KiB), 5-8 peers into bf16
+// -2.8 to +12.3.  Into bf16 with 1-4 peers it lost up to 18.6% (2 peers),
+// so those, and every launch below 1 MiB, keep the deeper tile.
+#ifndef FP8Q_RED_SMALL_U
+#define FP8Q_RED_SMALL_U 1
+#endif
+#ifndef FP8Q_RED_SMALL_U_FROM_N
+#define FP8Q_RED_SMALL_U_FROM_N (1ull << 19)
+#endif
+template <int K, bool BF16>
+constexpr int reduce_small_u() {
+  return (K <= 8 && (!BF16 || K >= 5)) ? FP8Q_RED_SMALL_U : reduce_u<K, BF16>();
+}
 
 // From 2 to 8 peers, launches of FP8Q_RED_T1_BELOW_N up to (not including)
 // FP8Q_RED_VS_BELOW_N elements take the vector scales (each lane loads its
@@ -436,6 +455,16 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
     constexpr uint32_t lds = (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0;
     const dim3 grid(grid_for_tiles((full + T - 1) / T, W));
     if (n < FP8Q_RED_T1_BELOW_N) {
+      constexpr int SU = reduce_small_u<K, BF16>();
+      if constexpr (SU != U) {
+        if (n >= FP8Q_RED_SMALL_U_FROM_N) {
+          const uint64_t sfull = n / ((uint64_t)SU * 256);
+          hipLaunchKernelGGL((reduce_kernel<FMT, K, SU, 1, BF16>),
+                             dim3(grid_for_tiles(sfull, W)), dim3(64 * W), lds, stream, P, y, n,
+                             sfull);
+          return hipGetLastError();
+        }
+      }
       hipLaunchKernelGGL((reduce_kernel<FMT, K, U, 1, BF16>), dim3(grid_for_tiles(full, W)),
                          dim3(64 * W), lds, stream, P, y, n, full);
       return hipGetLastError();

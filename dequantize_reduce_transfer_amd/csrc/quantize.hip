@@ -179,11 +179,21 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #ifndef FP8Q_QUANT_MID_W
 #define FP8Q_QUANT_MID_W 4
 #endif
-// Below FP8Q_QUANT_T1_BELOW_N elements a wave takes one tile, not T: at a
-// 1 MiB payload 2.5-2.6 us against 3.05-3.12 us on MI355X (alternated in one
-// run), the same at 4 MiB, and 13% slower at 16 MiB.
+// Below FP8Q_QUANT_T1_BELOW_N elements (an 8 MiB payload) a wave takes one
+// tile of FP8Q_QUANT_SMALL_U loads, not T tiles of U: the grid has four
+// times the waves and each wave's serial chain (loads, quotients, stores) is
+// a quarter as long, which is what a small launch's time is made of.  On
+// MI355X (graph replay over rotating windows, alternated in one run, e5m2),
+// one tile of U = 2 took a 1 MiB payload from 3.05-3.12 us to 2.5-2.6 us;
+// one tile of U = 1 then gained 10% at 767 KiB, 6% at 2 MiB, 20% at 3.9 MiB,
+// 7.5% at 4 MiB and 9.7% at 6 MiB over it (and over the two-tile shape from
+// 4 MiB), and tied at 64 KiB.  From 8 MiB up it lost 11-12%, so larger
+// launches keep two tiles of U = 2.
 #ifndef FP8Q_QUANT_T1_BELOW_N
-#define FP8Q_QUANT_T1_BELOW_N (1ull << 21)
+#define FP8Q_QUANT_T1_BELOW_N (1ull << 22)
+#endif
+#ifndef FP8Q_QUANT_SMALL_U
+#define FP8Q_QUANT_SMALL_U 1
 #endif
 #ifndef FP8Q_QUANT_MID_C
 #define FP8Q_QUANT_MID_C FP8Q_XCD_CHUNK
@@ -412,7 +422,11 @@ hipError_t launch_t(const void *x, uint64_t n, void *q, float *scales, hipStream
           launch_split<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream)))
       launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C>(x, n, q, scales, full, stream);
   } else {
-    launch_shape<FMT, FP8Q_QUANT_MID_W, FP8Q_QUANT_MID_C, 1>(x, n, q, scales, full, stream);
+    constexpr int SU = FP8Q_QUANT_SMALL_U, W = FP8Q_QUANT_MID_W;
+    const uint64_t sfull = n / ((uint64_t)SU * kWave * 8);
+    hipLaunchKernelGGL((quantize_kernel<FMT, SU, 1, W, FP8Q_QUANT_MID_C>),
+                       dim3(grid_for_tiles(sfull, W)), dim3(64 * W), 0, stream,
+                       static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales, n, sfull);
   }
   return hipGetLastError();
 }

@@ -159,12 +159,13 @@ def test_scale_outputs_at_odd_word_offsets_split_shapes(n):
     assert b[0] == -2.5 and np.all(b[1 + nb:] == -2.5)
 
 
-@pytest.mark.parametrize("n", [(1 << 21) - 1, 1 << 21, (1 << 23) - 1, (1 << 23) + 77,
+@pytest.mark.parametrize("n", [(1 << 22) - 1, 1 << 22, (1 << 23) - 1, (1 << 23) + 77,
                                (3 << 24) - 1, (3 << 24) + 77])
 def test_shape_switch_sizes(n):
-    """The launch shape changes at 2^21 elements (two tiles per wave), at
-    2^23 (a one-tile tail of 4096 tiles) and at 3 * 2^24 (one-wave
-    workgroups): one element either side of each (ragged above), e5m2,
+    """The launch shape changes at 2^22 elements (below, one tile of one
+    load per wave; from there, two tiles of two loads), at 2^23 (a one-tile
+    tail of 4096 tiles) and at 3 * 2^24 (one-wave workgroups): one element
+    either side of each (ragged above), e5m2,
     every code and scale against the oracle.  A
     gradient with planted blocks near both ends -- bf16 subnormals (amax
     below 2^-60), an inf, a NaN, zeros -- so that waves take both the

@@ -311,17 +311,32 @@ def test_mid_size_every_peer_count(fmt, k):
     _check_reduce(qs, ss, fmt, dev, "mid-size k=%d" % k)
 
 
-@pytest.mark.parametrize("n", [(1 << 22) - 1, 1 << 22, (1 << 26) - 1, 1 << 26])
-def test_reduce_shape_switch_sizes(n):
-    """The launch shape changes at 2^22 elements (two tiles per wave) and at
-    2^26 (vector-scale loads end): one element either side of each, k = 8,
-    fp32 out, every output's bits against the oracle."""
+SWITCH_CASES = [((1 << 19) - 1, 8, False), (1 << 19, 8, False), (1 << 19, 5, True),
+                ((1 << 22) - 1, 8, False), (1 << 22, 8, False), ((1 << 26) - 1, 8, False),
+                (1 << 26, 8, False), ((1 << 22) - 1, 5, True), (1 << 22, 5, True),
+                ((1 << 22) - 1, 4, True), ((1 << 22) - 1, 1, False), (1 << 22, 1, False),
+                ((1 << 22) - 1, 1, True)]
+
+
+@pytest.mark.parametrize("n,k,bf16", SWITCH_CASES,
+                         ids=["n%d-k%d-%s" % (c[0], c[1], "bf16" if c[2] else "f32")
+                              for c in SWITCH_CASES])
+def test_reduce_shape_switch_sizes(n, k, bf16):
+    """The launch shape changes at 2^19 elements (from there up to 2^22, one
+    tile per wave of one 256-element group into fp32 and into bf16 from 5
+    peers), at 2^22 (below it one tile per wave, above it two) and at 2^26
+    (vector-scale loads end): one element either side of each, every
+    output's bits against the oracle."""
     dev = require_gpu()
-    k = 8
     shards = [workloads.random_wire_shard(n, seed=6000 + p, fmt=fq.E4M3) for p in range(k)]
     qh = [a.numpy() for a, _ in shards]
     sh = [b.numpy() for _, b in shards]
-    y = fq.fp8q_dequant_reduce([dev_u8(a, dev) for a in qh], [dev_f32(b, dev) for b in sh], fq.E4M3)
+    out = torch.bfloat16 if bf16 else torch.float32
+    y = fq.fp8q_dequant_reduce([dev_u8(a, dev) for a in qh], [dev_f32(b, dev) for b in sh],
+                               fq.E4M3, out_dtype=out)
     torch.cuda.synchronize()
-    assert_bytes_equal(f32_bits(host(y)), f32_bits(oracle.dequant_reduce(qh, sh, fq.E4M3)),
-                       "n=%d" % n)
+    want = oracle.dequant_reduce(qh, sh, fq.E4M3, out_bf16=bf16)
+    if bf16:
+        assert_bf16_parity(host(y), want, "n=%d k=%d" % (n, k))
+    else:
+        assert_bytes_equal(f32_bits(host(y)), f32_bits(want), "n=%d k=%d" % (n, k))

@@ -363,6 +363,15 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 #ifndef FP8Q_RED8_C
 #define FP8Q_RED8_C 16
 #endif
+// Below FP8Q_RED8_T1_BELOW_N elements (a 32 MiB payload) each wave takes one
+// tile, not two: on MI355X (alternated in one run, % of 8 TB/s, 9 / 12 / 16
+// peers) 767 KiB 14.4 / 16.5 / 18.0 -> 17.9 / 21.1 / 27.3, 2 MiB 33.5 /
+// 38.0 / 41.3 -> 35.9 / 42.1 / 50.6, 16 MiB 67.9 / 71.3 / 72.1 -> 71.4 /
+// 73.7 / 76.4, 24 MiB 72.5 / 75.1 / 75.8 -> 76.3 / 77.8 / 79.8; tied at
+// 32 MiB.
+#ifndef FP8Q_RED8_T1_BELOW_N
+#define FP8Q_RED8_T1_BELOW_N (1ull << 24)
+#endif
 
 // Below FP8Q_RED_T1_BELOW_N elements each wave takes one tile, not T: the
 // grid has twice the waves and each wave's serial chain (loads, sums,
@@ -805,6 +814,27 @@ constexpr int requant8_u() {
 #ifndef FP8Q_XCD_CHUNK_RQ
 #define FP8Q_XCD_CHUNK_RQ 16     // XCD run (workgroups) of the requantize
 #endif
+// Small launches: below FP8Q_RQ8_T1_BELOW_N elements (FP8Q_RQ8_T1_BELOW_N_K4
+// from 4 peers) each wave takes one tile of one 512-element group
+// (FP8Q_RQ8_SMALL_U), not two tiles of two: four times the waves, each with
+// a quarter of the serial chain.  Two-tile waves left small launches with
+// a few hundred waves on 256 CUs.  On MI355X (graph replay over rotating
+// windows, alternated in one run, e4m3 -> e4m3, % of 8 TB/s) at a 767 KiB
+// payload: 1 peer 2.4 -> 4.5, 8 peers 6.1 -> 15.0, 16 peers 8.0 -> 22.9;
+// 2 MiB: 8 peers 21.5 -> 30.3; 7.9 MiB: 8 peers 52.2 -> 59.3; from 4 peers
+// also at 16 MiB (8 peers 62.5 -> 73.1) and 24 MiB (70.6 -> 74.4), tied at
+// 32 MiB and lower from there.  With 1 and 2 peers it lost 6-21% at 12-16
+// MiB, hence the lower bound below 4 peers.  One-wave workgroups measured
+// within a few percent either way.
+#ifndef FP8Q_RQ8_T1_BELOW_N
+#define FP8Q_RQ8_T1_BELOW_N (1ull << 22)
+#endif
+#ifndef FP8Q_RQ8_T1_BELOW_N_K4
+#define FP8Q_RQ8_T1_BELOW_N_K4 (1ull << 24)
+#endif
+#ifndef FP8Q_RQ8_SMALL_U
+#define FP8Q_RQ8_SMALL_U 1
+#endif
 
 template <int FIN, int FOUT, int K>
 void launch_requant8(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStream_t stream) {
@@ -814,6 +844,16 @@ void launch_requant8(const PeerPtrs &P, uint64_t n, void *qo, float *so, hipStre
   const uint64_t full = n / ((uint64_t)U * 512);
   constexpr uint64_t kTail = FP8Q_RQ8_TAIL_TILES;
   constexpr uint64_t C = FP8Q_XCD_CHUNK_RQ;
+  constexpr uint64_t kT1Below = K >= 4 ? (uint64_t)FP8Q_RQ8_T1_BELOW_N_K4
+                                       : (uint64_t)FP8Q_RQ8_T1_BELOW_N;
+  if (n < kT1Below) {
+    constexpr int SU = FP8Q_RQ8_SMALL_U;
+    const uint64_t sfull = n / ((uint64_t)SU * 512);
+    hipLaunchKernelGGL((requant8_kernel<FIN, FOUT, K, SU, 1, W, FP8Q_XCD_CHUNK_RQ>),
+                       dim3(grid_for_tiles(sfull, W)), dim3(64 * W), 0, stream, P,
+                       static_cast<u32x2 *>(qo), so, n, sfull);
+    return;
+  }
   if constexpr (T == 2 && kTail > 0 && K >= FP8Q_RQ8_TAIL_MIN_K) {
     if (full >= 2 * kTail) {
       const uint64_t q2 = (full - kTail) / (2 * W) / C * C;
@@ -877,6 +917,11 @@ template <int FMT, int K, bool BF16>
 hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = FP8Q_RED8_U, T = FP8Q_RED8_T, W = FP8Q_RED8_W;
   const uint64_t full = n / ((uint64_t)U * 512);
+  if (n < FP8Q_RED8_T1_BELOW_N) {
+    hipLaunchKernelGGL((reduce8_kernel<FMT, K, U, 1, BF16, W, FP8Q_RED8_C>),
+                       dim3(grid_for_tiles(full, W)), dim3(64 * W), 0, stream, P, y, n, full);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((reduce8_kernel<FMT, K, U, T, BF16, W, FP8Q_RED8_C>),
                      dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P, y,
                      n, full);
@@ -1021,11 +1066,31 @@ constexpr int mx_reduce_u() {
   return (K == 1 && !BF16) ? FP8Q_MX_U1_F32 : (K <= 8 ? peers_u<K>() : 1);
 }
 
+// Small launches from FP8Q_MXR_SMALL_MIN_K peers: below FP8Q_MXR_T1_BELOW_N
+// elements (a 4 MiB payload) each wave takes one tile of one 256-element
+// group, not two tiles of two.  On MI355X (alternated in one run, % change
+// at 256 KiB / 768 KiB / 2 MiB): 4 peers into fp32 +12 / +13 / +9, 8 peers
+// +24 / +20 / +2.5, into bf16 +16 / +12 / +9 and +29 / +20 / +6.5.  At 4 MiB
+// it lost 4-8%, and with one shard it changed nothing up to 4 MiB.
+#ifndef FP8Q_MXR_T1_BELOW_N
+#define FP8Q_MXR_T1_BELOW_N (1ull << 21)
+#endif
+#ifndef FP8Q_MXR_SMALL_MIN_K
+#define FP8Q_MXR_SMALL_MIN_K 4
+#endif
 template <int K, bool BF16>
 hipError_t launch_mx_reduce_t(const MxPeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = mx_reduce_u<K, BF16>();
   constexpr int T = FP8Q_RED_T;
   const uint64_t full = n / ((uint64_t)U * 256);
+  if constexpr (K >= FP8Q_MXR_SMALL_MIN_K) {
+    if (n < FP8Q_MXR_T1_BELOW_N) {
+      const uint64_t sfull = n / 256;
+      hipLaunchKernelGGL((mx_reduce_kernel<K, 1, 1, BF16>), dim3(grid_for_tiles(sfull)),
+                         dim3(256), 0, stream, P, y, n, sfull);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((mx_reduce_kernel<K, U, T, BF16>), dim3(grid_for_tiles((full + T - 1) / T)),
                      dim3(256), 0, stream, P, y, n, full);
   return hipGetLastError();

@@ -259,6 +259,18 @@ __global__ __launch_bounds__(64 * W) void mx8_split_kernel(const u32x4 *__restri
 // 8 TB/s with 4096 tiles (2048 and 8192: 83.7-83.9%).  The 4-wave shape
 // below that keeps mx8_kernel: there the same tails moved 32-128 MiB
 // tensors by -1.8 to +1.7 points.
+// Below FP8Q_MX8_T1_BELOW_N elements (an 8 MiB payload) each wave takes one
+// tile of one load (FP8Q_MX8_SMALL_U), not two tiles of two, as the block
+// quantize does: four times the waves, each with a quarter of the serial
+// chain.  On MI355X (alternated in one run, % change) +15% at a 768 KiB
+// payload, +10% at 2 MiB, +2.4% at 4 MiB, +1% at 7.9 MiB; the same shape up
+// to 32 MiB lost 6-9% at 16-24 MiB.
+#ifndef FP8Q_MX8_T1_BELOW_N
+#define FP8Q_MX8_T1_BELOW_N (1ull << 22)
+#endif
+#ifndef FP8Q_MX8_SMALL_U
+#define FP8Q_MX8_SMALL_U 1
+#endif
 #ifndef FP8Q_MX8_TAIL_TILES
 #define FP8Q_MX8_TAIL_TILES 4096
 #endif
@@ -291,6 +303,12 @@ hipError_t launch_mx8_quantize(const void *w, uint64_t n, void *q, void *e8m0,
       hipLaunchKernelGGL((mx8_kernel<U, T, 1, 256>), dim3(grid_for_tiles((full + T - 1) / T, 1)),
                          dim3(64), FP8Q_MX8_W1_LDS, stream, static_cast<const u32x4 *>(w),
                          static_cast<u32x2 *>(q), static_cast<uint8_t *>(e8m0), nchunks, full);
+  } else if (n < FP8Q_MX8_T1_BELOW_N) {
+    constexpr int SU = FP8Q_MX8_SMALL_U;
+    const uint64_t sfull = nchunks / ((uint64_t)SU * kWave);
+    hipLaunchKernelGGL((mx8_kernel<SU, 1, 4, FP8Q_XCD_CHUNK>), dim3(grid_for_tiles(sfull, 4)),
+                       dim3(256), 0, stream, static_cast<const u32x4 *>(w),
+                       static_cast<u32x2 *>(q), static_cast<uint8_t *>(e8m0), nchunks, sfull);
   } else {
     hipLaunchKernelGGL((mx8_kernel<U, T, 4, FP8Q_XCD_CHUNK>),
                        dim3(grid_for_tiles((full + T - 1) / T, 4)), dim3(256), 0, stream,

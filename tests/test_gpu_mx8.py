@@ -138,6 +138,17 @@ def test_scale_pointer_at_byte_offsets_one_wave_shape(offset):
     assert np.all(b[:offset] == 0xA5) and np.all(b[offset + ne:] == 0xA5)
 
 
+@pytest.mark.parametrize("rows", [2047, 2048])
+def test_small_launch_switch_sizes(rows):
+    """Below 2^22 elements the MXFP8 quantize takes one tile of one load per
+    wave: [2047, 2048] and [2048, 2048] weights, every code and E8M0 byte
+    against the oracle."""
+    dev = require_gpu()
+    K = 2048
+    w = workloads.kaiming_uniform((rows, K), seed=rows, device=dev)
+    _check(workloads.bits(w).reshape(rows, K), dev, "rows=%d" % rows)
+
+
 @pytest.mark.parametrize("rows", [(1 << 16) - 1, 1 << 16])
 def test_shape_switch_sizes(rows):
     """The MXFP8 launch changes shape at 2^27 elements (one-wave workgroups

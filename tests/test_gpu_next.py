@@ -141,6 +141,28 @@ def test_mx8_reduce_every_peer_count(k):
             _nan_aware_f32(y.ravel(), want.ravel(), "k=%d f32" % k)
 
 
+MXR_SWITCH = [(1023, 2048, 4), (1024, 2048, 4), (1023, 2048, 8), (1024, 2048, 3)]
+
+
+@pytest.mark.parametrize("rows,K,k", MXR_SWITCH, ids=["r%d-K%d-k%d" % c for c in MXR_SWITCH])
+def test_mx8_reduce_small_launch_switch(rows, K, k):
+    """From 4 peers, below 2^21 elements the MXFP8 receiver takes one tile
+    of one group per wave: [1023, 2048] and [1024, 2048] shards (and 3
+    peers, which keep the deeper tile), fp32 and bf16, against the oracle."""
+    dev = require_gpu()
+    shards = [oracle.mx8_quantize(workloads.bits(workloads.kaiming_uniform((rows, K), seed=720 + p))
+                                  .reshape(rows, K)) for p in range(k)]
+    qd = [dev_u8(a, dev) for a, _ in shards]
+    ed = [dev_u8(b, dev) for _, b in shards]
+    for dt, bf in ((torch.float32, False), (torch.bfloat16, True)):
+        y = host(fq.mx8_dequant_reduce(qd, ed, out_dtype=dt))
+        want = oracle.mx8_dequant_reduce([a for a, _ in shards], [b for _, b in shards], out_bf16=bf)
+        if bf:
+            assert_bf16_parity(y.ravel(), want.ravel(), "rows=%d k=%d bf16" % (rows, k))
+        else:
+            _nan_aware_f32(y.ravel(), want.ravel(), "rows=%d k=%d f32" % (rows, k))
+
+
 @pytest.mark.parametrize("rows,K", [(1, 32), (3, 96), (9, 256), (64, 2048), (129, 768)])
 def test_mx8_dequantize_ragged_leaves_canaries(rows, K):
     dev = require_gpu()
@@ -264,6 +286,22 @@ def test_requantize_quotient_across_every_scale_range(fmt_out):
     q_o, s_o = oracle.reduce_requantize(qs, ss, fq.E4M3, fmt_out)
     assert_bytes_equal(host(q_g), q_o, "codes")
     assert_bytes_equal(f32_bits(host(s_g)), f32_bits(s_o), "scales")
+
+
+RQ_SWITCH = [((1 << 22) - 1, 2), (1 << 22, 2), ((1 << 22) + 77, 3), ((1 << 24) - 1, 8),
+             (1 << 24, 8), ((1 << 24) - 1, 16)]
+
+
+@pytest.mark.parametrize("n,k", RQ_SWITCH, ids=["n%d-k%d" % c for c in RQ_SWITCH])
+def test_requantize_shape_switch_sizes(n, k):
+    """Below 2^22 elements (2^24 from 4 peers) the requantize takes one tile
+    of one 512-element group per wave; above, two tiles of two (ending in
+    one-tile waves from 4 peers): one element either side of each switch,
+    e4m3 -> e5m2, every code and scale against the oracle."""
+    dev = require_gpu()
+    shards = [workloads.random_wire_shard(n, seed=950 + 10 * k + p, fmt=0) for p in range(k)]
+    _check_requant([a.numpy() for a, _ in shards], [b.numpy() for _, b in shards], 0, 1, dev,
+                   "switch n=%d k=%d" % (n, k))
 
 
 @pytest.mark.parametrize("k", [4, 8, 16])

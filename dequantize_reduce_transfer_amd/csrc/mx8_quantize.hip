@@ -259,6 +259,10 @@ __global__ __launch_bounds__(64 * W) void mx8_split_kernel(const u32x4 *__restri
 // 8 TB/s with 4096 tiles (2048 and 8192: 83.7-83.9%).  The 4-wave shape
 // below that keeps mx8_kernel: there the same tails moved 32-128 MiB
 // tensors by -1.8 to +1.7 points.
+#ifndef FP8Q_MX8_TAIL_TILES
+#define FP8Q_MX8_TAIL_TILES 4096
+#endif
+
 // Below FP8Q_MX8_T1_BELOW_N elements (an 8 MiB payload) each wave takes one
 // tile of one load (FP8Q_MX8_SMALL_U), not two tiles of two, as the block
 // quantize does: four times the waves, each with a quarter of the serial
@@ -270,9 +274,6 @@ __global__ __launch_bounds__(64 * W) void mx8_split_kernel(const u32x4 *__restri
 #endif
 #ifndef FP8Q_MX8_SMALL_U
 #define FP8Q_MX8_SMALL_U 1
-#endif
-#ifndef FP8Q_MX8_TAIL_TILES
-#define FP8Q_MX8_TAIL_TILES 4096
 #endif
 
 // The split launch when it applies (full >= 2 * tail, grid under the cap).

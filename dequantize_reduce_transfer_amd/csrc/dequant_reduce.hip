@@ -390,17 +390,38 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 // payloads): 8 peers into fp32 +1.6 / +7.0 / +2.2 / +0.3 / +8.3, one shard
 // into fp32 -1.9 / +3.7 / +8.9 / +18.0 / +22.2, 2-7 peers into fp32 -5.5 to
 // +15.0 (gains from 2 MiB, up to 2.2% lost at 767 KiB), 5-8 peers into bf16
-// -2.8 to +12.3.  Into bf16 with 1-4 peers it lost up to 18.6% (2 peers),
-// so those, and every launch below 1 MiB, keep the deeper tile.
+// -2.8 to +12.3; 14 and 16 peers into fp32 (whose deeper tile is U = 2)
+// +96 / +67 / +39 / +60% and +101 / +51 / +30 / +53% at 1 / 2 / 4 /
+// 7.9 MiB.  Into bf16 with 1-4 peers it lost up to 18.6% (2 peers), so
+// those, and every launch below 1 MiB, keep the deeper tile.
 #ifndef FP8Q_RED_SMALL_U
 #define FP8Q_RED_SMALL_U 1
 #endif
 #ifndef FP8Q_RED_SMALL_U_FROM_N
 #define FP8Q_RED_SMALL_U_FROM_N (1ull << 19)
 #endif
+// Into fp32 the same one-group, one-tile waves also won at mid sizes: from
+// FP8Q_RED_F32_ONE_FROM_N elements (a 32 MiB payload; FP8Q_RED_F32_ONE_FROM_N_K9
+// from 9 peers) up to FP8Q_RED_F32_ONE_BELOW_N (256 MiB), against the
+// vector-scale, one-tile-tail and two-tile shapes there.  On MI355X
+// (alternated in one run, points of 8 TB/s): 8 peers +0.7 / +2.0 / +2.7 /
+// +1.4 at 32 / 48 / 96 / 192 MiB, 2 peers +2.8 to +3.0 from 32 MiB, 3 and
+// 5-7 peers +0.1 to +2.4, 9-16 peers +0.3 to +11.8 from 8 MiB; 4 peers lost
+// up to 1.9, so they keep their shapes.  At 437.5M elements per peer the
+// two-tile shape won again (82.5% against 81.1% at 8 peers), hence the
+// upper bound.
+#ifndef FP8Q_RED_F32_ONE_FROM_N
+#define FP8Q_RED_F32_ONE_FROM_N (1ull << 24)
+#endif
+#ifndef FP8Q_RED_F32_ONE_FROM_N_K9
+#define FP8Q_RED_F32_ONE_FROM_N_K9 (1ull << 22)
+#endif
+#ifndef FP8Q_RED_F32_ONE_BELOW_N
+#define FP8Q_RED_F32_ONE_BELOW_N (1ull << 27)
+#endif
 template <int K, bool BF16>
 constexpr int reduce_small_u() {
-  return (K <= 8 && (!BF16 || K >= 5)) ? FP8Q_RED_SMALL_U : reduce_u<K, BF16>();
+  return (!BF16 || K >= 5) ? FP8Q_RED_SMALL_U : reduce_u<K, BF16>();
 }
 
 // From 2 to 8 peers, launches of FP8Q_RED_T1_BELOW_N up to (not including)
@@ -463,6 +484,17 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
     constexpr int W = reduce_waves<K, BF16>();
     constexpr uint32_t lds = (K == 1 && BF16) ? FP8Q_DEQ_BF16_LDS : 0;
     const dim3 grid(grid_for_tiles((full + T - 1) / T, W));
+    if constexpr (!BF16 && K >= 2 && K != 4) {
+      // fp32 mid sizes: one-group tiles, one per wave (FP8Q_RED_F32_ONE_*)
+      constexpr uint64_t kFrom = K >= 9 ? (uint64_t)FP8Q_RED_F32_ONE_FROM_N_K9
+                                        : (uint64_t)FP8Q_RED_F32_ONE_FROM_N;
+      if (n >= kFrom && n < FP8Q_RED_F32_ONE_BELOW_N) {
+        const uint64_t sfull = n / 256;
+        hipLaunchKernelGGL((reduce_kernel<FMT, K, 1, 1, BF16>), dim3(grid_for_tiles(sfull, W)),
+                           dim3(64 * W), lds, stream, P, y, n, sfull);
+        return hipGetLastError();
+      }
+    }
     if (n < FP8Q_RED_T1_BELOW_N) {
       constexpr int SU = reduce_small_u<K, BF16>();
       if constexpr (SU != U) {

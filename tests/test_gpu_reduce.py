@@ -315,7 +315,10 @@ SWITCH_CASES = [((1 << 19) - 1, 8, False), (1 << 19, 8, False), (1 << 19, 5, Tru
                 ((1 << 22) - 1, 8, False), (1 << 22, 8, False), ((1 << 26) - 1, 8, False),
                 (1 << 26, 8, False), ((1 << 22) - 1, 5, True), (1 << 22, 5, True),
                 ((1 << 22) - 1, 4, True), ((1 << 22) - 1, 1, False), (1 << 22, 1, False),
-                ((1 << 22) - 1, 1, True), ((1 << 24) - 1, 12, True), (1 << 24, 12, True)]
+                ((1 << 22) - 1, 1, True), ((1 << 24) - 1, 12, True), (1 << 24, 12, True),
+                ((1 << 24) - 1, 8, False), (1 << 24, 8, False), (1 << 24, 4, False),
+                ((1 << 22) - 1, 12, False), (1 << 22, 12, False), ((1 << 27) - 1, 2, False),
+                (1 << 27, 2, False)]
 
 
 @pytest.mark.parametrize("n,k,bf16", SWITCH_CASES,
@@ -325,9 +328,11 @@ def test_reduce_shape_switch_sizes(n, k, bf16):
     """The launch shape changes at 2^19 elements (from there up to 2^22, one
     tile per wave of one 256-element group into fp32 and into bf16 from 5
     peers), at 2^22 (below it one tile per wave, above it two), at 2^26
-    (vector-scale loads end) and, into bf16 from 9 peers (eight codes per
-    lane), at 2^24 (one tile per wave below): one element either side of
-    each, every output's bits against the oracle."""
+    (vector-scale loads end), into bf16 from 9 peers (eight codes per
+    lane) at 2^24 (one tile per wave below), and into fp32 at 2^24 (2^22
+    from 9 peers) and 2^27, the bounds of the one-group, one-tile band (not
+    taken by 4 peers): one element either side of each, every output's bits
+    against the oracle."""
     dev = require_gpu()
     shards = [workloads.random_wire_shard(n, seed=6000 + p, fmt=fq.E4M3) for p in range(k)]
     qh = [a.numpy() for a, _ in shards]

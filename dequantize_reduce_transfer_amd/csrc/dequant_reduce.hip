@@ -372,6 +372,27 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 #ifndef FP8Q_RED8_T1_BELOW_N
 #define FP8Q_RED8_T1_BELOW_N (1ull << 24)
 #endif
+// From FP8Q_RED8_MIN_K_LARGE peers into bf16 the eight-codes mapping also
+// takes launches from FP8Q_RED8_LARGE_FROM_N (a 64 MiB payload) up to
+// FP8Q_RED8_LARGE_BELOW_N (256 MiB), one tile per wave below
+// FP8Q_RED8_T1_BELOW_N_LARGE, in place of the vector-scale, one-tile-tail
+// and per-wave shapes.  On MI355X (alternated in one run, points of 8 TB/s
+// at 64 / 96 / 128 / 200 MiB): 8 peers +2.2 / +1.8 / +0.4 / +1.2, 5-7
+// peers +0.1 to +1.8; at 32-48 MiB within 0.3.  In the bench the full
+// stress payload went from 79.7-80.0% to 81.7-81.8%; at 218.75M elements
+// per peer it was 0.2-0.3 points lower, hence the upper bound.
+#ifndef FP8Q_RED8_MIN_K_LARGE
+#define FP8Q_RED8_MIN_K_LARGE 5
+#endif
+#ifndef FP8Q_RED8_LARGE_FROM_N
+#define FP8Q_RED8_LARGE_FROM_N (1ull << 25)
+#endif
+#ifndef FP8Q_RED8_LARGE_BELOW_N
+#define FP8Q_RED8_LARGE_BELOW_N (1ull << 27)
+#endif
+#ifndef FP8Q_RED8_T1_BELOW_N_LARGE
+#define FP8Q_RED8_T1_BELOW_N_LARGE (1ull << 26)
+#endif
 
 // Below FP8Q_RED_T1_BELOW_N elements each wave takes one tile, not T: the
 // grid has twice the waves and each wave's serial chain (loads, sums,
@@ -477,6 +498,11 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
   if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_BF16) {
     return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
   } else {
+    if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_LARGE) {
+      // into bf16 from 5 peers, FP8Q_RED8_LARGE_FROM_N <= n < FP8Q_RED8_LARGE_BELOW_N
+      if (n >= FP8Q_RED8_LARGE_FROM_N && n < FP8Q_RED8_LARGE_BELOW_N)
+        return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
+    }
     constexpr int U = reduce_u<K, BF16>();
     constexpr int T = reduce_t<K, BF16>();
     const uint64_t tile = (uint64_t)U * 256;
@@ -949,7 +975,9 @@ template <int FMT, int K, bool BF16>
 hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   constexpr int U = FP8Q_RED8_U, T = FP8Q_RED8_T, W = FP8Q_RED8_W;
   const uint64_t full = n / ((uint64_t)U * 512);
-  if (n < FP8Q_RED8_T1_BELOW_N) {
+  constexpr uint64_t kT1Below = K >= FP8Q_RED8_MIN_K_BF16 ? (uint64_t)FP8Q_RED8_T1_BELOW_N
+                                                          : (uint64_t)FP8Q_RED8_T1_BELOW_N_LARGE;
+  if (n < kT1Below) {
     hipLaunchKernelGGL((reduce8_kernel<FMT, K, U, 1, BF16, W, FP8Q_RED8_C>),
                        dim3(grid_for_tiles(full, W)), dim3(64 * W), 0, stream, P, y, n, full);
     return hipGetLastError();

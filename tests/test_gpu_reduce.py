@@ -318,7 +318,9 @@ SWITCH_CASES = [((1 << 19) - 1, 8, False), (1 << 19, 8, False), (1 << 19, 5, Tru
                 ((1 << 22) - 1, 1, True), ((1 << 24) - 1, 12, True), (1 << 24, 12, True),
                 ((1 << 24) - 1, 8, False), (1 << 24, 8, False), (1 << 24, 4, False),
                 ((1 << 22) - 1, 12, False), (1 << 22, 12, False), ((1 << 27) - 1, 2, False),
-                (1 << 27, 2, False)]
+                (1 << 27, 2, False), ((1 << 25) - 1, 6, True), (1 << 25, 6, True),
+                ((1 << 26) - 1, 5, True), (1 << 26, 5, True), ((1 << 27) - 1, 5, True),
+                (1 << 27, 5, True)]
 
 
 @pytest.mark.parametrize("n,k,bf16", SWITCH_CASES,
@@ -331,7 +333,9 @@ def test_reduce_shape_switch_sizes(n, k, bf16):
     (vector-scale loads end), into bf16 from 9 peers (eight codes per
     lane) at 2^24 (one tile per wave below), and into fp32 at 2^24 (2^22
     from 9 peers) and 2^27, the bounds of the one-group, one-tile band (not
-    taken by 4 peers): one element either side of each, every output's bits
+    taken by 4 peers), and into bf16 from 5 peers at 2^25, 2^26 and 2^27,
+    where the eight-codes mapping takes over (one tile per wave below 2^26)
+    and hands back: one element either side of each, every output's bits
     against the oracle."""
     dev = require_gpu()
     shards = [workloads.random_wire_shard(n, seed=6000 + p, fmt=fq.E4M3) for p in range(k)]

@@ -378,11 +378,12 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 // FP8Q_RED8_T1_BELOW_N_LARGE, in place of the vector-scale, one-tile-tail
 // and per-wave shapes.  On MI355X (alternated in one run, points of 8 TB/s
 // at 64 / 96 / 128 / 200 MiB): 8 peers +2.2 / +1.8 / +0.4 / +1.2, 5-7
-// peers +0.1 to +1.8; at 32-48 MiB within 0.3.  In the bench the full
-// stress payload went from 79.7-80.0% to 81.7-81.8%; at 218.75M elements
-// per peer it was 0.2-0.3 points lower, hence the upper bound.
+// peers +0.1 to +1.8, 2-4 peers +0.2 to +2.9; at 32-48 MiB within 0.3.  In
+// the bench the full stress payload went from 79.7-80.0% to 81.7-81.8%; at
+// 218.75M elements per peer it was 0.2-0.3 points lower, hence the upper
+// bound.
 #ifndef FP8Q_RED8_MIN_K_LARGE
-#define FP8Q_RED8_MIN_K_LARGE 5
+#define FP8Q_RED8_MIN_K_LARGE 2
 #endif
 #ifndef FP8Q_RED8_LARGE_FROM_N
 #define FP8Q_RED8_LARGE_FROM_N (1ull << 25)
@@ -499,7 +500,7 @@ hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t s
     return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
   } else {
     if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_LARGE) {
-      // into bf16 from 5 peers, FP8Q_RED8_LARGE_FROM_N <= n < FP8Q_RED8_LARGE_BELOW_N
+      // into bf16, FP8Q_RED8_LARGE_FROM_N <= n < FP8Q_RED8_LARGE_BELOW_N
       if (n >= FP8Q_RED8_LARGE_FROM_N && n < FP8Q_RED8_LARGE_BELOW_N)
         return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
     }

@@ -319,6 +319,7 @@ SWITCH_CASES = [((1 << 19) - 1, 8, False), (1 << 19, 8, False), (1 << 19, 5, Tru
                 ((1 << 24) - 1, 8, False), (1 << 24, 8, False), (1 << 24, 4, False),
                 ((1 << 22) - 1, 12, False), (1 << 22, 12, False), ((1 << 27) - 1, 2, False),
                 (1 << 27, 2, False), ((1 << 25) - 1, 6, True), (1 << 25, 6, True),
+                ((1 << 25) - 1, 3, True), (1 << 25, 3, True),
                 ((1 << 26) - 1, 5, True), (1 << 26, 5, True), ((1 << 27) - 1, 5, True),
                 (1 << 27, 5, True)]
 
@@ -333,7 +334,7 @@ def test_reduce_shape_switch_sizes(n, k, bf16):
     (vector-scale loads end), into bf16 from 9 peers (eight codes per
     lane) at 2^24 (one tile per wave below), and into fp32 at 2^24 (2^22
     from 9 peers) and 2^27, the bounds of the one-group, one-tile band (not
-    taken by 4 peers), and into bf16 from 5 peers at 2^25, 2^26 and 2^27,
+    taken by 4 peers), and into bf16 from 2 peers at 2^25, 2^26 and 2^27,
     where the eight-codes mapping takes over (one tile per wave below 2^26)
     and hands back: one element either side of each, every output's bits
     against the oracle."""

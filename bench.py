@@ -479,9 +479,11 @@ def host_latency_us(torch, fn, reps=50):
 
 def payload_sweep(torch, fq, workloads, dev, reps=20):
     """e5m2 block quantize and k = 8 fused reduce (fp32 out) at the payload
-    sizes of the sweep, each launch on a different window of 2 GiB pools so
-    that the timed bytes come from HBM, not the 256 MB Infinity Cache.
-    Times are per launch of a graph of back-to-back launches; payloads up to
+    sizes of the sweep, each launch on a different window of 2 GiB pools.
+    From 16 MiB (quantize) and 4 MiB (reduce) payloads up, the 20 windows of
+    one graph span more than the 256 MB Infinity Cache, so the timed bytes
+    come from HBM; below that they fit in it, and those launch-bound points
+    may be served from the cache.  Times are per launch of a graph of back-to-back launches; payloads up to
     4 MiB also get the host's enqueue-to-completion latency of one call."""
     n_pool = 1 << 30
     x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)

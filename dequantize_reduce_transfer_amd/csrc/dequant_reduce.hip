@@ -482,7 +482,8 @@ constexpr int reduce_small_u() {
 #define FP8Q_RED_TAIL_MIN_K 4
 #endif
 
-// Dynamic LDS the single-shard dequantize into bf16 reserves per workgroup
+// Dynamic LDS the single-shard dequantize into bf16 (below FP8Q_DEQ8_FROM_N
+// elements, where it still takes reduce_kernel) reserves per workgroup
 // (the kernel uses none), so that at most 6 of its 4-wave workgroups share a
 // CU: 437.5M elements took 206.5-207.8 us capped against 212.7-213.9 us
 // uncapped (80.0% against 77.7% of 8 TB/s, alternated in one run on
@@ -490,15 +491,45 @@ constexpr int reduce_small_u() {
 #ifndef FP8Q_DEQ_BF16_LDS
 #define FP8Q_DEQ_BF16_LDS 24576
 #endif
+// The single-shard dequantize into bf16 from FP8Q_DEQ8_FROM_N elements up,
+// except from FP8Q_DEQ8_GAP_FROM_N up to (not including)
+// FP8Q_DEQ8_GAP_BELOW_N, takes the eight-codes mapping of reduce8_kernel
+// (one 8-byte code load and one 16-byte bf16 store per lane) with one
+// 512-element tile per wave (launch_deq8_t), in place of the four-codes
+// kernel above.  On MI355X (graph replay, alternated in one run, % of
+// 8 TB/s, with the data in HBM: windows totalling 768 MB or more per graph,
+// three times the Infinity Cache): 1 / 2 / 4 / 6 / 7.9 MiB payloads +1.1 /
+// +2.3 / +3.5 / +2.7 / +4.2 points; 22 / 24 / 32 / 48 MiB +3.5 / +5.3 /
+// +5.3 / +3.8; 64 / 128 / 224 MiB +5.3 / +3.4 / +2.1; 218.75M elements
+// (417 MiB) +0.5; at 0.75 MiB even.  From 8 MiB to 20 MiB it lost 1.8-8.0
+// points (18 MiB: 60.7 against 52.7), which is the gap.  Into fp32 the same
+// mapping lost 4-21 points at every size (its two 16-byte stores per lane
+// leave each store instruction strided), so fp32 keeps its shape.
+#ifndef FP8Q_DEQ8_FROM_N
+#define FP8Q_DEQ8_FROM_N (1ull << 19)
+#endif
+#ifndef FP8Q_DEQ8_GAP_FROM_N
+#define FP8Q_DEQ8_GAP_FROM_N (1ull << 22)
+#endif
+#ifndef FP8Q_DEQ8_GAP_BELOW_N
+#define FP8Q_DEQ8_GAP_BELOW_N (11ull << 20)
+#endif
 
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream);
+template <int FMT, bool BF16>
+hipError_t launch_deq8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream);
 
 template <int FMT, int K, bool BF16>
 hipError_t launch_reduce_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
   if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_BF16) {
     return launch_reduce8_t<FMT, K, BF16>(P, n, y, stream);
   } else {
+    if constexpr (K == 1 && BF16) {
+      // the single-shard dequantize into bf16 from FP8Q_DEQ8_FROM_N elements
+      if (n >= FP8Q_DEQ8_FROM_N && (n < FP8Q_DEQ8_GAP_FROM_N || n >= FP8Q_DEQ8_GAP_BELOW_N))
+        return launch_deq8_t<FMT, BF16>(P, n, y, stream);
+    }
     if constexpr (BF16 && K >= FP8Q_RED8_MIN_K_LARGE) {
       // into bf16, FP8Q_RED8_LARGE_FROM_N <= n < FP8Q_RED8_LARGE_BELOW_N
       if (n >= FP8Q_RED8_LARGE_FROM_N && n < FP8Q_RED8_LARGE_BELOW_N)
@@ -986,6 +1017,15 @@ hipError_t launch_reduce8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t 
   hipLaunchKernelGGL((reduce8_kernel<FMT, K, U, T, BF16, W, FP8Q_RED8_C>),
                      dim3(grid_for_tiles((full + T - 1) / T, W)), dim3(64 * W), 0, stream, P, y,
                      n, full);
+  return hipGetLastError();
+}
+
+template <int FMT, bool BF16>
+hipError_t launch_deq8_t(const PeerPtrs &P, uint64_t n, void *y, hipStream_t stream) {
+  constexpr int W = FP8Q_RED8_W;
+  const uint64_t full = n / 512;
+  hipLaunchKernelGGL((reduce8_kernel<FMT, 1, 1, 1, BF16, W, FP8Q_RED8_C>),
+                     dim3(grid_for_tiles(full, W)), dim3(64 * W), 0, stream, P, y, n, full);
   return hipGetLastError();
 }
 

@@ -179,18 +179,21 @@ __device__ void quantize_tail(const uint16_t *__restrict__ x, uint8_t *__restric
 #ifndef FP8Q_QUANT_MID_W
 #define FP8Q_QUANT_MID_W 4
 #endif
-// Below FP8Q_QUANT_T1_BELOW_N elements (an 8 MiB payload) a wave takes one
-// tile of FP8Q_QUANT_SMALL_U loads, not T tiles of U: the grid has four
-// times the waves and each wave's serial chain (loads, quotients, stores) is
-// a quarter as long, which is what a small launch's time is made of.  On
-// MI355X (graph replay over rotating windows, alternated in one run, e5m2),
-// one tile of U = 2 took a 1 MiB payload from 3.05-3.12 us to 2.5-2.6 us;
-// one tile of U = 1 then gained 10% at 767 KiB, 6% at 2 MiB, 20% at 3.9 MiB,
-// 7.5% at 4 MiB and 9.7% at 6 MiB over it (and over the two-tile shape from
-// 4 MiB), and tied at 64 KiB.  From 8 MiB up it lost 11-12%, so larger
-// launches keep two tiles of U = 2.
+// Below FP8Q_QUANT_T1_BELOW_N elements (up to 7168 tiles of 512, a 7 MiB
+// payload) a wave takes one tile of FP8Q_QUANT_SMALL_U loads, not T tiles
+// of U: the grid has four times the waves and each wave's serial chain
+// (loads, quotients, stores) is a quarter as long, which is what a small
+// launch's time is made of.  On MI355X (graph replay, alternated in one run,
+// e5m2, over 20 windows that the 256 MB Infinity Cache holds at these
+// sizes), one tile of U = 2 took a 1 MiB payload from 3.05-3.12 us to
+// 2.5-2.6 us; one tile of U = 1 then gained 10% at 767 KiB, 6% at 2 MiB,
+// 20% at 3.9 MiB, 7.5% at 4 MiB and 9.7% at 6 MiB over it, and tied at
+// 64 KiB.  With the data in HBM (windows totalling 768 MB per graph), it
+// gained 2.4-3.9 points of 8 TB/s at 4-7 MiB and 1.3-2.5 at 0.75-2 MiB, and
+// lost 3.2-4.4 points from 7.25 MiB up: 7168 one-tile waves are 28 per CU,
+// the kernel's occupancy, so a larger launch needs a second round of waves.
 #ifndef FP8Q_QUANT_T1_BELOW_N
-#define FP8Q_QUANT_T1_BELOW_N (1ull << 22)
+#define FP8Q_QUANT_T1_BELOW_N (7168ull * 512 + 1)
 #endif
 #ifndef FP8Q_QUANT_SMALL_U
 #define FP8Q_QUANT_SMALL_U 1

@@ -159,7 +159,8 @@ def test_scale_outputs_at_odd_word_offsets_split_shapes(n):
     assert b[0] == -2.5 and np.all(b[1 + nb:] == -2.5)
 
 
-@pytest.mark.parametrize("n", [(1 << 22) - 1, 1 << 22, (1 << 23) - 1, (1 << 23) + 77,
+@pytest.mark.parametrize("n", [7168 * 512, 7168 * 512 + 1, (1 << 22) - 1, 1 << 22,
+                               (1 << 23) - 1, (1 << 23) + 77,
                                (3 << 24) - 1, (3 << 24) + 77])
 def test_shape_switch_sizes(n):
     """The launch shape changes at 2^22 elements (below, one tile of one

@@ -320,6 +320,8 @@ SWITCH_CASES = [((1 << 19) - 1, 8, False), (1 << 19, 8, False), (1 << 19, 5, Tru
                 ((1 << 22) - 1, 12, False), (1 << 22, 12, False), ((1 << 27) - 1, 2, False),
                 (1 << 27, 2, False), ((1 << 25) - 1, 6, True), (1 << 25, 6, True),
                 ((1 << 25) - 1, 3, True), (1 << 25, 3, True),
+                ((1 << 19) - 1, 1, True), (1 << 19, 1, True), (1 << 22, 1, True),
+                ((11 << 20) - 1, 1, True), (11 << 20, 1, True), (3 * (1 << 25) + 77, 1, True),
                 ((1 << 26) - 1, 5, True), (1 << 26, 5, True), ((1 << 27) - 1, 5, True),
                 (1 << 27, 5, True)]
 
@@ -336,8 +338,10 @@ def test_reduce_shape_switch_sizes(n, k, bf16):
     from 9 peers) and 2^27, the bounds of the one-group, one-tile band (not
     taken by 4 peers), and into bf16 from 2 peers at 2^25, 2^26 and 2^27,
     where the eight-codes mapping takes over (one tile per wave below 2^26)
-    and hands back: one element either side of each, every output's bits
-    against the oracle."""
+    and hands back, and where one shard into bf16 takes it with one tile per
+    wave from 2^19, leaves it at 2^22 and takes it again at 11 * 2^20 (with a
+    ragged tail at 3 * 2^25 + 77): one element either side of each, every
+    output's bits against the oracle."""
     dev = require_gpu()
     shards = [workloads.random_wire_shard(n, seed=6000 + p, fmt=fq.E4M3) for p in range(k)]
     qh = [a.numpy() for a, _ in shards]

@@ -415,7 +415,11 @@ __global__ __launch_bounds__((64 * reduce_waves<K, BF16>())) void reduce_split_k
 // -2.8 to +12.3; 14 and 16 peers into fp32 (whose deeper tile is U = 2)
 // +96 / +67 / +39 / +60% and +101 / +51 / +30 / +53% at 1 / 2 / 4 /
 // 7.9 MiB.  Into bf16 with 1-4 peers it lost up to 18.6% (2 peers), so
-// those, and every launch below 1 MiB, keep the deeper tile.
+// those, and every launch below 1 MiB, keep the deeper tile.  The one-shard
+// figures come from windows that the 256 MB Infinity Cache holds; with the
+// data in HBM (768 MB of windows per graph) one shard into fp32 measured
+// +3.9 / +4.5 / +3.8 / +3.1 points of 8 TB/s at 2 / 4 / 6 / 7.9 MiB against
+// two-tile waves of the wider tile.
 #ifndef FP8Q_RED_SMALL_U
 #define FP8Q_RED_SMALL_U 1
 #endif
@@ -915,7 +919,10 @@ constexpr int requant8_u() {
 // also at 16 MiB (8 peers 62.5 -> 73.1) and 24 MiB (70.6 -> 74.4), tied at
 // 32 MiB and lower from there.  With 1 and 2 peers it lost 6-21% at 12-16
 // MiB, hence the lower bound below 4 peers.  One-wave workgroups measured
-// within a few percent either way.
+// within a few percent either way.  With 1 peer the windows of those runs
+// fit in the 256 MB Infinity Cache; with the data in HBM (768 MB of windows
+// per graph) it measured +1.4 / +0.8 / +1.0 points at 2 / 4 / 6 MiB and
+// -0.4 at 7.9 MiB.
 #ifndef FP8Q_RQ8_T1_BELOW_N
 #define FP8Q_RQ8_T1_BELOW_N (1ull << 22)
 #endif

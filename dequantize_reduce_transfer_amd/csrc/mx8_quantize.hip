@@ -268,7 +268,10 @@ __global__ __launch_bounds__(64 * W) void mx8_split_kernel(const u32x4 *__restri
 // quantize does: four times the waves, each with a quarter of the serial
 // chain.  On MI355X (alternated in one run, % change) +15% at a 768 KiB
 // payload, +10% at 2 MiB, +2.4% at 4 MiB, +1% at 7.9 MiB; the same shape up
-// to 32 MiB lost 6-9% at 16-24 MiB.
+// to 32 MiB lost 6-9% at 16-24 MiB.  Measured again with the data in HBM
+// (windows totalling 768 MB per graph, three times the Infinity Cache, which
+// holds the 20 windows of those runs at these sizes): +1.5 / +1.3 / +2.2 /
+// +0.6 points of 8 TB/s at 2 / 4 / 6 / 7.9 MiB.
 #ifndef FP8Q_MX8_T1_BELOW_N
 #define FP8Q_MX8_T1_BELOW_N (1ull << 22)
 #endif

@@ -163,6 +163,27 @@ def test_mx8_reduce_small_launch_switch(rows, K, k):
             _nan_aware_f32(y.ravel(), want.ravel(), "rows=%d k=%d f32" % (rows, k))
 
 
+@pytest.mark.parametrize("rows,K", [(255, 2048), (256, 2048), (1365, 768), (4099, 160)])
+def test_mx8_dequantize_bf16_every_byte(rows, K):
+    """The MXFP8 dequantize into bf16 at [255, 2048], [256, 2048] (2^19
+    elements) and ragged [1365, 768] and [4099, 160]: every code byte and
+    E8M0 byte drawn (NaN codes, the NaN scale 0xFF and the scale floor 0x00
+    included), canaries after the output, every bf16 against the oracle."""
+    dev = require_gpu()
+    rng = np.random.default_rng(rows + K)
+    q = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+    e = rng.integers(0, 256, (rows, K // 32)).astype(np.uint8)
+    n = rows * K
+    y_big = torch.full((n + 40,), -2.5, dtype=torch.bfloat16, device=dev)
+    fq.mx8_dequantize(dev_u8(q, dev), dev_u8(e, dev), out_dtype=torch.bfloat16,
+                      out=y_big[:n].view(rows, K))
+    torch.cuda.synchronize()
+    yh = host(y_big)
+    assert_bf16_parity(yh[:n], oracle.mx8_dequantize(q, e, out_bf16=True).ravel(),
+                       "mx dequantize bf16 %dx%d" % (rows, K))
+    assert np.all(yh[n:] == 0xC020)
+
+
 @pytest.mark.parametrize("rows,K", [(1, 32), (3, 96), (9, 256), (64, 2048), (129, 768)])
 def test_mx8_dequantize_ragged_leaves_canaries(rows, K):
     dev = require_gpu()

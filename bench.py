@@ -477,13 +477,25 @@ def host_latency_us(torch, fn, reps=50):
     return round(ts[len(ts) // 2] * 1e6, 1)
 
 
+SWEEP_GRAPH_BYTES = 768e6   # bytes one sweep graph touches: 3x the Infinity Cache
+SWEEP_MAX_LAUNCHES = 8192
+
+
+def sweep_launches(bytes_per_launch, reps):
+    """Launches per sweep graph: at least `reps`, and enough that one replay
+    touches SWEEP_GRAPH_BYTES, so a window's bytes are long gone from the
+    256 MB Infinity Cache when the next replay comes back to it."""
+    need = int(SWEEP_GRAPH_BYTES // bytes_per_launch) + 1
+    return max(reps, min(need, SWEEP_MAX_LAUNCHES))
+
+
 def payload_sweep(torch, fq, workloads, dev, reps=20):
     """e5m2 block quantize and k = 8 fused reduce (fp32 out) at the payload
     sizes of the sweep, each launch on a different window of 2 GiB pools.
-    From 16 MiB (quantize) and 4 MiB (reduce) payloads up, the 20 windows of
-    one graph span more than the 256 MB Infinity Cache, so the timed bytes
-    come from HBM; below that they fit in it, and those launch-bound points
-    may be served from the cache.  Times are per launch of a graph of back-to-back launches; payloads up to
+    Each graph holds at least `reps` launches, and at small payloads enough
+    more (sweep_launches) that its windows total 768 MB, three times the
+    256 MB Infinity Cache, so the timed bytes come from HBM at every size.
+    Times are per launch of a graph of back-to-back launches; payloads up to
     4 MiB also get the host's enqueue-to-completion latency of one call."""
     n_pool = 1 << 30
     x = workloads.sweep_payload(2 * n_pool, seed=0, device=dev)
@@ -512,8 +524,10 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
             return lambda: fq.fp8q_dequant_reduce(qs, ss, fq.E5M2, out=y[yo:yo + n])
 
         q_runs, r_runs = [], []
-        qm = graph_ms(torch, [quant(i) for i in range(reps)], all_runs=q_runs)
-        rm = graph_ms(torch, [red(i) for i in range(reps)], all_runs=r_runs)
+        nq = sweep_launches(QUANT_BYTES_PER_ELEM * n, reps)
+        nr = sweep_launches(reduce_bytes_per_elem(8, 4) * n, reps)
+        qm = graph_ms(torch, [quant(i) for i in range(nq)], all_runs=q_runs)
+        rm = graph_ms(torch, [red(i) for i in range(nr)], all_runs=r_runs)
         row = {"payload_bytes": nbytes, "elements": n,
                "quantize_us": round(qm * 1e3, 2),
                "quantize_hbm_GBps": round(QUANT_BYTES_PER_ELEM * n / qm / 1e6, 1),
@@ -521,6 +535,7 @@ def payload_sweep(torch, fq, workloads, dev, reps=20):
                "reduce_k8_us": round(rm * 1e3, 2),
                "reduce_k8_hbm_GBps": round(reduce_bytes_per_elem(8, 4) * n / rm / 1e6, 1),
                "reduce_k8_bf16_equiv_GBps": round(16 * n / rm / 1e6, 1),
+               "quantize_launches_per_graph": nq, "reduce_k8_launches_per_graph": nr,
                "quantize_us_runs": [round(v * 1e3, 2) for v in q_runs],
                "reduce_k8_us_runs": [round(v * 1e3, 2) for v in r_runs]}
         if nbytes <= 4 << 20:

@@ -37,6 +37,20 @@ def test_cpu_pieces_tile_the_range(total, parts, multiple):
     assert min(total, starts[-1] + step) == total
 
 
+@pytest.mark.parametrize("nbytes", [65536, 262144, 785408, 4194304, 16777216, 67108864])
+def test_sweep_graphs_span_three_infinity_caches(nbytes):
+    """Each payload-sweep graph touches at least 768 MB (three times the
+    256 MB Infinity Cache) and holds at least the 20 launches asked for, up
+    to the launch cap, for the quantize and for the k = 8 reduce."""
+    n = nbytes // 2
+    for per_elem in (bench.QUANT_BYTES_PER_ELEM, bench.reduce_bytes_per_elem(8, 4)):
+        m = bench.sweep_launches(per_elem * n, 20)
+        assert m >= 20 and m <= max(20, bench.SWEEP_MAX_LAUNCHES)
+        assert m * per_elem * n >= bench.SWEEP_GRAPH_BYTES or m == bench.SWEEP_MAX_LAUNCHES
+    assert bench.sweep_launches(bench.QUANT_BYTES_PER_ELEM * 32768, 20) == 7732
+    assert bench.sweep_launches(bench.QUANT_BYTES_PER_ELEM * (1 << 25), 20) == 20
+
+
 def test_gates_flag_every_gated_point():
     ops = {"quantize_e4m3": {"frac_peak": 0.84}, "dequant_reduce_k8_f32": {"frac_peak": 0.80},
            "mx8_layer": {"frac_peak": 0.79}}
